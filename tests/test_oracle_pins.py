@@ -1,0 +1,147 @@
+"""Pins of the CPU oracle against what the pages and mathematics fix.
+
+Every oracle function is checked against something other than itself:
+hand-worked examples under ``tests/golden/`` (each cites its passage),
+closed forms, a library routine (PyTorch SDPA in float64 on the CPU) on the
+unsharded case, and pure-Python brute force on tiny inputs.
+``tests/test_oracle_mutations.py`` plants plausible mistakes in copies of the
+oracle and shows that these checks catch each one.
+"""
+
+import math
+
+import numpy as np
+import pytest
+
+import oracle as O
+from tests.conftest import load_golden
+from tests import pin_checks as P
+
+
+# ---------------------------------------------------------------- partition / pad
+
+def test_partition_golden():
+    P.check_partition(O)
+
+
+def test_padded_length_closed_form():
+    P.check_padded_length(O)
+
+
+def test_pad_tokens_bytes():
+    P.check_pad_tokens(O)
+
+
+def test_mask_extension_golden_and_properties():
+    P.check_mask_extension(O)
+
+
+# ---------------------------------------------------------------- head swap
+
+def test_relayout_golden():
+    P.check_relayout_golden(O)
+
+
+def test_relayout_brute_force():
+    P.check_relayout_brute_force(O)
+
+
+def test_relayout_round_trip_bytes():
+    P.check_relayout_round_trip(O)
+
+
+def test_relayout_shape_rule_and_identity():
+    P.check_relayout_shapes(O)
+
+
+# ---------------------------------------------------------------- attention
+
+def test_attention_golden():
+    P.check_attention_golden(O)
+
+
+def test_attention_brute_force():
+    P.check_attention_brute_force(O)
+
+
+def test_attention_matches_sdpa_float64():
+    P.check_attention_sdpa(O)
+
+
+def test_attention_closed_forms():
+    P.check_attention_closed_forms(O)
+
+
+def test_attention_garbage_pad_invariance():
+    P.check_garbage_pad_invariance(O)
+
+
+def test_attention_row_subset():
+    rng = np.random.default_rng(5)
+    q = rng.standard_normal((2, 37, 3, 8))
+    k = rng.standard_normal((2, 41, 3, 8))
+    v = rng.standard_normal((2, 41, 3, 8))
+    m = (rng.random((1, 37, 41)) < 0.6).astype(np.uint8)
+    full = O.attention_heads(q, k, v, 0.3, 39, m)
+    rows = np.array([0, 5, 36])
+    part = O.attention_heads(q, k, v, 0.3, 39, m, rows=rows)
+    assert np.array_equal(part[:, rows], full[:, rows])
+
+
+# ---------------------------------------------------------------- restore
+
+def test_gather_output_golden():
+    P.check_gather_output(O)
+
+
+# ---------------------------------------------------------------- whole path
+
+def test_sharded_equals_unsharded_self():
+    P.check_sharded_equals_unsharded_self(O)
+
+
+def test_sharded_equals_unsharded_user_mask():
+    P.check_sharded_equals_unsharded_mask(O)
+
+
+def test_sharded_equals_unsharded_cross():
+    P.check_sharded_equals_unsharded_cross(O)
+
+
+def test_pad_rows_finite_with_user_mask():
+    """Pad query rows and a fully masked real row stay finite (the NaN guard)."""
+    rng = np.random.default_rng(11)
+    b, t, h, d, w = 1, 10, 4, 4, 4          # T_pad = 12, two pad rows
+    q, k, v = (rng.standard_normal((b, t, h, d)) for _ in range(3))
+    m = (rng.random((b, t, t)) < 0.5).astype(np.uint8)
+    m[0, 3, :] = 0                          # a real row with nothing visible
+    out, inter = O.ulysses_self_attention(q, k, v, w, 0.5, user_mask=m, keep_intermediates=True)
+    assert np.isfinite(out).all()
+    assert np.isfinite(inter["o_heads"]).all()
+    assert np.all(out[0, 3] == 0.0)
+    # the pad query rows (10, 11) attend the real keys only: they equal plain
+    # attention over all 10 real keys with no user mask
+    mext = inter["mask"]
+    assert mext[0, 10:, :10].all() and not mext[0, 10:, 10:].any()
+
+
+def test_tiny_workload_against_brute_force():
+    """The 50-token workload (padded to 52, W=4) end to end, vs pure Python."""
+    from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS["tiny"]
+    x = make_inputs(wl)
+    q, k, v = (x[n].astype(np.float64) for n in "qkv")
+    scale = 1.0 / math.sqrt(wl.D)
+    out = O.ulysses_self_attention(q, k, v, wl.W, scale)
+    for h in (0, 3, 7):
+        ref = P.brute_attention(q[0, :, h].tolist(), k[0, :, h].tolist(), v[0, :, h].tolist(),
+                                scale, wl.T, None)
+        assert np.max(np.abs(out[0, :, h] - np.array(ref))) < 1e-12
+
+
+def test_bf16_widening():
+    bits = np.array([0x3F80, 0xC020, 0x0000, 0x8000, 0x7F7F, 0x0001], dtype=np.uint16)
+    got = O.bf16_bits_to_f64(bits)
+    want = [1.0, -2.5, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133]
+    assert got.tolist() == want
+    assert math.copysign(1.0, got[3]) < 0
