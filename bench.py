@@ -1,0 +1,301 @@
+"""Benchmark one step of the sequence-parallel attention path on one MI355X.
+
+A step is the whole path over one batch of synthetic input, all W virtual
+ranks per launch: pad -> partition -> send_recv_heads (Q, K, V in one launch)
+-> masked attention on every rank's local heads -> gather_heads ->
+gather_output_tokens.  Inputs are resident in HBM before the timed region.
+
+Prints one JSON line.  ``value`` is masked-attention TFLOP/s of the whole step
+(algorithmic attention flops per step / step time); the per-kernel figures,
+the attention roofline and the head-relayout bandwidth are added beside it.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config video_self]
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "masked-attention TFLOP/s (MFMA util %) + head relayout GB/s (HBM %), 1 GPU"
+PEAK_BF16_TFLOPS = 2500.0      # MI355X dense bf16 MFMA
+PEAK_F32_MFMA_TFLOPS = 157.3   # MI355X fp32 matrix
+PEAK_HBM_GBS = 8000.0          # MI355X HBM3E
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def kernel_hash(*names) -> str:
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "sequence_attention_video_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str, src_hash: str):
+    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
+    if it was taken on the current kernel source; else None."""
+    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path, encoding="utf-8").read()
+    m = re.search(r"^traffic_json:\s*(\{.*\})\s*$", text, flags=re.M)
+    if not m:
+        return None
+    rec = json.loads(m.group(1))
+    if rec.get("kernel_source_hash") != src_hash:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="video_self")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        msg = ("bench.py measures one GPU only: the W ranks of the sequence-parallel path are virtual "
+               "ranks on a single device in this build; multi-GPU runs are not supported")
+        if int(os.environ.get("RANK", "0")) == 0:
+            print(msg, file=sys.stderr, flush=True)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    from sequence_attention_video_amd import binding
+    from sequence_attention_video_amd.pipeline import UlyssesStep
+    from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
+
+    binding.load()          # fails loudly if the HIP library is missing
+    wl = WORKLOADS[args.config]
+    dev = torch.device("cuda:0")
+    log("inputs", wl.name)
+    x = make_inputs(wl)
+
+    def to_dev(a):
+        t = torch.from_numpy(a)
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    mask = to_dev(x["mask"]) if x["mask"] is not None else None
+    step = UlyssesStep(wl, q, k, v, mask, device=dev)
+    B, H, D, W, T, Tp, Hl = wl.B, wl.H, wl.D, wl.W, wl.T, wl.T_pad, wl.Hl
+    eb = wl.eb
+
+    # -- algorithmic work per step
+    step.run()
+    torch.cuda.synchronize()
+    if wl.cross:
+        pairs_per_bh = wl.Tq * T
+        tq = wl.Tq
+    elif mask is not None:
+        pairs_per_bh = int(step.mask_ext.to(torch.int64).sum().item()) // step.mask_ext.shape[0]
+        tq = Tp
+    else:
+        pairs_per_bh = Tp * T
+        tq = Tp
+    attn_flops = 4 * D * H * B * pairs_per_bh                       # all W rank shares
+    n_relayed = 2 if wl.cross else 3
+    relayout_bytes = 2 * n_relayed * B * Tp * H * D * eb            # read + write, Q/K/V (K/V for cross)
+    relayout_o_bytes = 2 * B * tq * H * D * eb
+    out_rows = wl.Tq if wl.cross else T
+    gather_bytes = 2 * B * out_rows * H * D * eb
+    pad_bytes = (n_relayed * B * (T + Tp) * H * D * eb) if step.need_pad else 0
+    if step.need_pad and mask is not None:
+        pad_bytes += mask.shape[0] * (T * T + Tp * Tp)
+
+    # -- warmup, then K timed steps with per-stage events on the launch stream
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    log("timed", args.steps)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t_start.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        e[0].record(stream)
+        step.pad()
+        _, lengths = step.partition()
+        step.send_recv_heads()
+        e[1].record(stream)
+        step.attention()
+        e[2].record(stream)
+        step.gather_heads()
+        e[3].record(stream)
+        step.gather_output_tokens(lengths)
+        e[4].record(stream)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    stage = lambda a, b: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(args.steps)]))
+    ms_pad_send = stage(0, 1)
+    ms_attn = stage(1, 2)
+    ms_gh = stage(2, 3)
+    ms_gather = stage(3, 4)
+
+    # -- relayout bandwidth with rotating buffer sets (> 1 GB in flight defeats the 256 MB MALL)
+    set_bytes = relayout_bytes
+    nsets = max(2, int(math.ceil(1.2e9 / max(set_bytes, 1))))
+    nsets = min(nsets, 16)
+    dt = step.kh.dtype
+    tok_shape = (B, Tp, H, D)
+    head_shape = (W, B, Tp, Hl, D)
+    sets = [([torch.empty(tok_shape, dtype=dt, device=dev) for _ in range(n_relayed)],
+             [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(n_relayed)]) for _ in range(nsets)]
+    for s_, _ in sets:
+        for t in s_:
+            t.view(torch.uint8).random_()
+    tok_view = (Tp // W * H * D, Tp * H * D)
+    rl_iters = max(args.steps, 2 * nsets)
+    for i in range(nsets):
+        binding.sp_relayout_heads(sets[i][0], sets[i][1], W, B, Tp, H, D, binding.SP_TOKENS_TO_HEADS,
+                                  tok_strides=tok_view)
+    torch.cuda.synchronize()
+    r0 = torch.cuda.Event(enable_timing=True)
+    r1 = torch.cuda.Event(enable_timing=True)
+    r0.record(stream)
+    for i in range(rl_iters):
+        s_, d_ = sets[i % nsets]
+        binding.sp_relayout_heads(s_, d_, W, B, Tp, H, D, binding.SP_TOKENS_TO_HEADS, tok_strides=tok_view)
+    r1.record(stream)
+    torch.cuda.synchronize()
+    ms_relayout_rot = r0.elapsed_time(r1) / rl_iters
+    del sets
+    torch.cuda.empty_cache()
+
+    # -- oracle-free sanity on the timed buffers (parity proper lives in tests/)
+    finite = bool(torch.isfinite(step.out.float()).all().item())
+    back = torch.empty_like(step.kp)
+    binding.sp_relayout_heads([step.kh], [back], W, B, Tp, H, D, binding.SP_HEADS_TO_TOKENS, tok_strides=tok_view)
+    torch.cuda.synchronize()
+    round_trip = bool(torch.equal(back.view(torch.uint8), step.kp.view(torch.uint8)))
+
+    src_hash = kernel_hash("sp_attention.hip", "sp_internal.h")
+    peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
+    attn_tflops = attn_flops / (ms_attn * 1e-3) / 1e12
+    traffic = read_traffic(wl.name, src_hash)
+    roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                "frac": round(attn_tflops / peak_mfma, 4), "traffic": traffic,
+                "kernel": "attn_%s_kernel<%d>" % (wl.dtype, D), "flops_per_launch": attn_flops,
+                "avg_launch_ms": round(ms_attn, 4)}
+    gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
+    kernels = {
+        "pad+send_recv_heads": {"ms": round(ms_pad_send, 4), "bytes": pad_bytes + relayout_bytes},
+        "send_recv_heads_rotating": {"ms": round(ms_relayout_rot, 4), "bytes": relayout_bytes,
+                                     "GB/s": round(gbs(relayout_bytes, ms_relayout_rot), 1),
+                                     "hbm_frac": round(gbs(relayout_bytes, ms_relayout_rot) / PEAK_HBM_GBS, 4),
+                                     "buffer_sets": nsets},
+        "masked_attention": {"ms": round(ms_attn, 4), "TFLOP/s": round(attn_tflops, 2),
+                             "mfma_frac": round(attn_tflops / peak_mfma, 4)},
+        "gather_heads": {"ms": round(ms_gh, 4), "bytes": relayout_o_bytes,
+                         "GB/s": round(gbs(relayout_o_bytes, ms_gh), 1)},
+        "gather_output_tokens": {"ms": round(ms_gather, 4), "bytes": gather_bytes,
+                                 "GB/s": round(gbs(gather_bytes, ms_gather), 1)},
+    }
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, x, args.cpu_seconds)
+
+    value = attn_flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": wl.dtype,
+        "data": "synthetic",
+        "config": {"workload": wl.name, "B": B, "T": T, "T_pad": Tp, "W": W, "H": H, "Hl": Hl, "D": D,
+                   "mask": wl.mask, "cross": wl.cross, "Tq": wl.Tq if wl.cross else T},
+        "roofline": roofline,
+        "relayout": {"achieved": kernels["send_recv_heads_rotating"]["GB/s"], "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": kernels["send_recv_heads_rotating"]["hbm_frac"]},
+        "cpu_baseline": cpu,
+        "kernels": kernels,
+        "attention_flops_per_step": attn_flops,
+        "wall_s_timed": round(wall, 3),
+        "checks": {"output_finite": finite, "relayout_round_trip_bytes_equal": round_trip},
+        "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(wl, x, budget_s: float):
+    """The oracle as it stands, timed on the host on a bounded sample of the same
+    workload: rank 0's local heads, query rows in blocks of 256, all keys."""
+    import numpy as np
+
+    import oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # noqa: BLE001
+        threads = len(os.sched_getaffinity(0))
+    D, T, Tp, W, Hl = wl.D, wl.T, wl.T_pad, wl.W, wl.Hl
+    scale = 1.0 / math.sqrt(D)
+    widen = (lambda a: O.bf16_bits_to_f64(a)) if wl.dtype == "bf16" else (lambda a: a.astype(np.float64))
+    mask = None if x["mask"] is None else O.extend_user_mask(x["mask"], Tp)[0]
+    flops = 0
+    rows_done = 0
+    heads_done = []
+    t0 = time.perf_counter()
+    for j in range(Hl):                          # rank 0 owns heads 0..Hl-1
+        kj = widen(O.pad_tokens(x["k"][:, :, j], Tp)[0]) if not wl.cross else widen(
+            O.pad_tokens(x["k"][:, :, j], Tp)[0])
+        vj = widen(O.pad_tokens(x["v"][:, :, j], Tp)[0])
+        qsrc = x["q"][0, :, j] if wl.cross else O.pad_tokens(x["q"][:, :, j], Tp)[0]
+        nq = qsrc.shape[0]
+        kv_valid = T if mask is None else Tp
+        for i0 in range(0, nq, 256):
+            i1 = min(nq, i0 + 256)
+            mrows = None if mask is None else mask[i0:i1]
+            O.attention(widen(qsrc[i0:i1]), kj, vj, scale, kv_valid, mrows)
+            vis = (i1 - i0) * min(kv_valid, kj.shape[0]) if mrows is None else int(mrows[:, :kv_valid].sum())
+            flops += 4 * D * vis
+            rows_done += i1 - i0
+            if time.perf_counter() - t0 > budget_s:
+                break
+        heads_done.append(j)
+        if time.perf_counter() - t0 > budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{rows_done} query rows of rank 0's heads {heads_done} against all "
+                      f"{Tp} keys, float64 NumPy oracle, {dt:.1f} s",
+            "seconds": round(dt, 2)}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,181 @@
+/*
+ * sp.h -- C ABI of libspattn.so: the Ulysses-style sequence-parallel attention
+ * hot path for audio-video diffusion transformers, on one AMD MI355X (gfx950).
+ *
+ * Sources (page title, then the section on it):
+ *   [SP] "LTX-2 序列并行拆解：token 切分、all2all 换头与 runner 接入全链路",
+ *        section "token 切片、换头、gather 还原" and its steps 补齐 (pad),
+ *        切分 (partition), 换头 (head swap), 还原 (restore); section
+ *        "全局注意力没有变，只是分布方式变了" (invariants).
+ *   [MG] "Multi-GPU Inference" (LTX-2 multigpu README), table "Capabilities".
+ *
+ * One GPU holds all W ranks ("virtual ranks"): rank r's buffers are slices of
+ * one allocation, addressed through a rank stride.  The exchange between ranks
+ * becomes an on-device relayout.
+ *
+ * Conventions for every entry point:
+ *   - Pointers named as device pointers are device memory owned by the caller;
+ *     arrays named as host arrays are host memory owned by the caller.  The
+ *     library allocates nothing, frees nothing and keeps no state between
+ *     calls.
+ *   - All GPU work is enqueued on `stream` (a hipStream_t; NULL = the null
+ *     stream) and returns without synchronising.  A device fault surfaces at
+ *     the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is launched.  On
+ *     any error status nothing is written and nothing is launched.
+ *   - Strides and sizes are in elements, not bytes, unless named *_bytes.
+ *   - Element types: SP_F32 (4-byte float) and SP_BF16 (bfloat16 stored as 2
+ *     bytes).  Copies (pad, relayout, gather) move bytes and never round.
+ *   - Source and destination buffers of one call must not overlap, except
+ *     where an entry point says otherwise.
+ */
+#ifndef SP_H
+#define SP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  SP_OK = 0,
+  SP_ERR_NOT_DIVISIBLE = 1, /* a token count does not divide by the world size ([SP] 切分) */
+  SP_ERR_INVALID_ARG = 2,   /* null pointer, bad size, bad stride, inconsistent counts */
+  SP_ERR_UNSUPPORTED = 3,   /* valid request outside the built set (head dim, dtype) */
+  SP_ERR_HIP = 4            /* the HIP runtime refused a launch */
+} sp_status;
+
+typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
+
+typedef enum {
+  SP_TOKENS_TO_HEADS = 0, /* send_recv_heads ([SP] 换头) */
+  SP_HEADS_TO_TOKENS = 1  /* gather_heads   ([SP] 换头, the swap back) */
+} sp_dir;
+
+/* Where the W rank shards of one tensor sit in memory: rank r, batch b start
+ * at base + r*rank + b*batch (elements).  Token rows inside a shard are packed. */
+typedef struct {
+  int64_t rank;
+  int64_t batch;
+} sp_shard_strides;
+
+/* Strides of a (rank, batch, token, head, d) view; d is contiguous. */
+typedef struct {
+  int64_t rank;
+  int64_t batch;
+  int64_t token;
+  int64_t head;
+} sp_attn_strides;
+
+/* Human-readable name of a status (static storage; never NULL). */
+const char* sp_status_string(sp_status status);
+
+/* Version of the library, as major*10000 + minor*100 + patch. */
+int32_t sp_version(void);
+
+/*
+ * sp_partition -- compute_sequence_partition ([SP] 切分).
+ * Splits `total_tokens` into `world_size` equal shards.  The total must divide
+ * evenly: otherwise SP_ERR_NOT_DIVISIBLE (the page's ValueError) and nothing is
+ * written.  world_size < 1 or total_tokens < 0 -> SP_ERR_INVALID_ARG.
+ * offsets, lengths: host arrays of world_size entries, or NULL to skip.
+ * Host only: launches nothing and needs no GPU.
+ */
+sp_status sp_partition(int64_t total_tokens, int32_t world_size, int64_t* offsets, int64_t* lengths);
+
+/*
+ * sp_pad -- pad_modality_for_uniform_sharding ([SP] 补齐).
+ * Tokens: y[b, t, :] = x[b, t, :] for t < T and zero bytes for T <= t < T_pad,
+ *   with x (B, T, C) at batch stride x_batch_stride (>= T*C) and y (B, T_pad,
+ *   C) packed.  x == y with x_batch_stride == T_pad*C pads in place (only the
+ *   tail rows are written).  x and y may both be NULL (mask only); x may be
+ *   NULL alone when T == 0 (y is then all zero bytes).
+ * User mask (optional; mask_in and mask_out both NULL or both non-NULL):
+ *   mask_in (B, T, T) uint8, 1 = may attend, packed; mask_out (B, T_pad, T_pad):
+ *   the T x T block is copied, pad key columns are 0 for every row, and pad
+ *   query rows see every real key and no pad key, so no row is left with
+ *   nothing visible.  With no user mask the caller uses the key-only mask
+ *   instead, i.e. kv_valid_len = T in sp_masked_attention.
+ * T_pad >= T is required (any value; divisibility is sp_partition's check).
+ * Errors: SP_ERR_INVALID_ARG for negative sizes, T_pad < T, a bad stride or an
+ * unpaired pointer; SP_ERR_UNSUPPORTED if C * element size is not a multiple
+ * of 16 bytes.
+ */
+sp_status sp_pad(const void* x, int64_t x_batch_stride, void* y, int64_t B, int64_t T, int64_t T_pad,
+                 int64_t C, sp_dtype dtype, const uint8_t* mask_in, uint8_t* mask_out, void* stream);
+
+/*
+ * sp_relayout_heads -- send_recv_heads / gather_heads ([SP] 换头).
+ * Token side of rank s: (B, Ts, H, D) with Ts = T_pad / W, at
+ *   base + s*tok.rank + b*tok.batch, rows of H*D packed.
+ * Head side of rank r: (B, T_pad, Hl, D) with Hl = H / W, at
+ *   base + r*head.rank + b*head.batch, rows of Hl*D packed.
+ * The map is head_r[b, s*Ts + t, j, :] = tok_s[b, t, r*Hl + j, :]: every rank
+ * ends up with every token of its Hl local heads.  SP_TOKENS_TO_HEADS reads the
+ * token side (src) and writes the head side (dst); SP_HEADS_TO_TOKENS is the
+ * exact inverse.  The round trip returns the input byte for byte.
+ * src, dst: host arrays of n_tensors device pointers (1..3 tensors, e.g. Q, K,
+ * V in one launch), all with the same shapes and strides.
+ * Errors: T_pad % W != 0 -> SP_ERR_NOT_DIVISIBLE; H % W != 0, n_tensors out of
+ * 1..3, W < 1, null or equal src/dst pointers, strides that make shards
+ * overlap -> SP_ERR_INVALID_ARG; Hl*D*element size not a multiple of 16 bytes
+ * -> SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                            int64_t B, int64_t T_pad, int32_t H, int32_t D, sp_dtype dtype, sp_dir dir,
+                            sp_shard_strides tok, sp_shard_strides head, void* stream);
+
+/*
+ * sp_masked_attention -- attention on the local heads ([SP] 换头, computed in
+ * place on each rank; masks as defined in [SP] 补齐).
+ * For R rank shares, B batches, Hl heads: query i attends key j iff
+ *   j < kv_valid_len, and, if mask != NULL, mask[b, i, j] != 0.
+ * o = softmax(scale * q k^T) v over the visible keys, accumulated in float32;
+ * a query row with no visible key gets 0 (never NaN).
+ * q: (R, B, Tq, Hl, D) with strides qs; k, v: (R, B, Tk, Hl, D) with ks, vs;
+ * o: (R, B, Tq, Hl, D) with os (o must not overlap q, k or v).  d is
+ * contiguous for all four.  Base pointers and strides must keep every 16-byte
+ * group of d aligned (bf16: multiples of 8 elements; f32: of 4).
+ * mask: device (B, Tq, Tk) uint8, rows packed (row stride Tk), batch stride
+ * mask_batch_stride (0 = one mask for every batch), or NULL for the key-only
+ * padding mask.  The mask is shared by every rank and head.
+ * workspace: device scratch of sp_masked_attention_workspace_size() bytes (the
+ * per-tile mask classes); may be NULL when that size is 0.
+ * Supported: SP_BF16 with D in {64, 128} (bf16 MFMA, float32 softmax and
+ * accumulation, output rounded to nearest even) and SP_F32 with D in
+ * {16, 64, 128} (float32 MFMA throughout).
+ * Errors: sizes < 0, null tensors, kv_valid_len < 0, workspace too small ->
+ * SP_ERR_INVALID_ARG; other D -> SP_ERR_UNSUPPORTED.
+ */
+size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
+                                          sp_dtype dtype, int32_t has_mask, int64_t mask_batch_stride);
+
+sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
+                              const void* v, sp_attn_strides vs, void* o, sp_attn_strides os, int32_t R,
+                              int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D, sp_dtype dtype,
+                              int64_t kv_valid_len, const uint8_t* mask, int64_t mask_batch_stride, float scale,
+                              void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * sp_gather_unpad -- gather_output_tokens ([SP] 还原).
+ * in: rank r's local output (B, Ts, C) at in + r*in_strides.rank +
+ *   b*in_strides.batch, rows of C packed.  Rank r keeps its first counts[r]
+ *   rows; the kept rows are concatenated in rank order and the first T of them
+ *   form out (B, T, C), packed.  With equal shards all ranks are already at the
+ *   longest length, so padding to it is a no-op.
+ * counts: host array of W entries, or NULL for Ts each.
+ * Errors: counts[r] outside 0..Ts, sum(counts) < T, negative sizes, null
+ * pointers -> SP_ERR_INVALID_ARG; C * element size not a multiple of 16 bytes
+ * -> SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_gather_unpad(const void* in, sp_shard_strides in_strides, void* out, int32_t W, int64_t B,
+                          int64_t Ts, int64_t C, const int64_t* counts, int64_t T, sp_dtype dtype,
+                          void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SP_H */

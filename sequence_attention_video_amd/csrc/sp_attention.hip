@@ -1,0 +1,547 @@
+// Masked attention on the local heads of every virtual rank, as one flash-style
+// kernel per dtype for gfx950 (CDNA4).
+//
+// Source: page "LTX-2 序列并行拆解：token 切分、all2all 换头与 runner 接入全链路",
+// section "token 切片、换头、gather 还原": step 换头 (after the swap each rank runs
+// full-sequence attention over its local heads) and step 补齐 (the key-only
+// padding mask, and the extended user mask in which pad query rows keep the real
+// keys visible).
+//
+// Design (bf16):
+//   * one workgroup = 4 waves = 128 query rows of one (rank, batch, head); each
+//     wave owns 32 query rows for the whole key loop;
+//   * key tiles of 64 are staged in LDS: K row-major, V transposed (V^T), both
+//     padded so the MFMA operand reads are bank-conflict free;
+//   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
+//     operand).  In the 32x32 accumulator layout a lane holds 16 keys of ONE
+//     query, so the row max/sum are in-lane plus one swap with lane^32, and the
+//     same registers, rounded to bf16, are directly the B operand of
+//     O^T += V^T P^T (second MFMA), whose accumulator again gives each lane one
+//     query: the softmax rescale is a per-lane scalar;
+//   * softmax in float32 with exp2 (scale*log2 e folded into one FMA); the
+//     running max is only raised when a tile's max exceeds it by more than 2^8,
+//     so the O rescale runs rarely while p stays <= 256 (exact in float32,
+//     representable in bf16);
+//   * user masks are classified once per call into empty/full/partial tiles:
+//     empty tiles are skipped, full tiles read no mask bytes;
+//   * workgroup ids are remapped so that the 8 XCDs each take a contiguous run
+//     of (rank, batch, head) groups: the q-tiles sharing one head's K/V run on
+//     the same XCD and share its L2.
+
+#include "sp_internal.h"
+
+#include <cmath>
+
+namespace sp {
+namespace {
+
+constexpr int BM = 128;              // query rows per workgroup
+constexpr int BN = 64;               // keys per tile
+constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+
+enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+
+struct AttnArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  int64_t qs[4], ks[4], vs[4], os[4];   // rank, batch, token, head strides (elements)
+  int64_t B, Tq, Tk;
+  int32_t Hl;
+  int64_t kv_end;                        // keys >= kv_end are never visible
+  const uint8_t* mask;                   // (B, Tq, Tk) or null
+  int64_t mask_bs;                       // batch stride of mask (0 = shared)
+  const uint8_t* cls;                    // tile classes (Bm, nqt, nkt)
+  int32_t nqt, nkt;
+  float c;                               // scale * log2(e)
+  uint32_t nwg;
+};
+
+// Workgroup i runs on XCD i % 8.  Give XCD x a contiguous range of logical
+// tiles so that neighbouring q-tiles of one head share that XCD's L2.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
+  const uint32_t x = i & 7u, j = i >> 3;
+  const uint32_t q = n >> 3, rr = n & 7u;
+  return x < rr ? x * (q + 1) + j : rr * (q + 1) + (x - rr) * q + j;
+}
+
+struct TileCoord {
+  int64_t r, b;
+  int32_t head, qt;
+};
+
+template <bool MASK>
+__device__ __forceinline__ TileCoord decode_tile(const AttnArgs& a) {
+  uint32_t rest = xcd_remap(blockIdx.x, a.nwg);
+  TileCoord t;
+  const uint32_t qi = rest % uint32_t(a.nqt);
+  rest /= uint32_t(a.nqt);
+  t.head = int32_t(rest % uint32_t(a.Hl));
+  rest /= uint32_t(a.Hl);
+  t.b = int64_t(rest % uint64_t(a.B));
+  t.r = int64_t(rest / uint64_t(a.B));
+  // with a user mask, later query tiles usually see more keys (causal-like
+  // masks): start those first
+  t.qt = MASK ? a.nqt - 1 - int32_t(qi) : int32_t(qi);
+  return t;
+}
+
+__device__ __forceinline__ float wave_max_pair(float x) {
+  return fmaxf(x, __shfl_xor(x, 32));
+}
+
+// ---------------------------------------------------------------- bf16 kernel
+
+template <int D, bool MASK>
+__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
+  static_assert(D % 32 == 0, "bf16 path needs D divisible by 32");
+  constexpr int KST = D + 8;     // K tile row stride (elements)
+  constexpr int VST = BN + 4;    // V^T tile row stride (elements)
+  constexpr int NKS = D / 16;    // k-steps of the QK^T MFMA
+  constexpr int NDB = D / 32;    // 32-row blocks of O^T
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KST];
+  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+
+  const TileCoord tc = decode_tile<MASK>(a);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const uint16_t* qp = static_cast<const uint16_t*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
+  const uint16_t* kp = static_cast<const uint16_t*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
+  const uint16_t* vp = static_cast<const uint16_t*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
+  uint16_t* op = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
+
+  const int64_t qrow = int64_t(tc.qt) * BM + w * 32 + l32;
+  const bool qvalid = qrow < a.Tq;
+
+  bf16x8 qf[NKS];
+#pragma unroll
+  for (int s = 0; s < NKS; ++s) {
+    qf[s] = bf16x8{};
+    if (qvalid) qf[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * a.qs[2] + 16 * s + 8 * h);
+  }
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+  float m_run = -1e30f;   // running max, log2 units (scaled score)
+  float l_run = 0.f;      // this lane's share of the softmax denominator
+
+  const uint8_t* cls_row = nullptr;
+  const uint8_t* mrow = nullptr;
+  if (MASK) {
+    const int64_t bm = a.mask_bs ? tc.b : 0;
+    cls_row = a.cls + (bm * a.nqt + tc.qt) * int64_t(a.nkt);
+    mrow = a.mask + tc.b * a.mask_bs + qrow * a.Tk;
+  }
+
+  const int nkt_eff = int((a.kv_end + BN - 1) / BN);
+  for (int kt = 0; kt < nkt_eff; ++kt) {
+    uint8_t cls = kTileFull;
+    if (MASK) {
+      cls = cls_row[kt];
+      if (cls == kTileEmpty) continue;
+    }
+    const int64_t key0 = int64_t(kt) * BN;
+    __syncthreads();   // every wave is done with the previous tile
+    // K tile, row-major
+#pragma unroll
+    for (int c = tid; c < BN * D / 8; c += kThreads) {
+      const int n = c / (D / 8), dc = c % (D / 8);
+      u32x4 val = u32x4{0, 0, 0, 0};
+      if (key0 + n < a.Tk) val = *reinterpret_cast<const u32x4*>(kp + (key0 + n) * a.ks[2] + 8 * dc);
+      *reinterpret_cast<u32x4*>(&k_lds[n * KST + 8 * dc]) = val;
+    }
+    // V tile, transposed: thread takes 4 keys x 8 dims and writes 8 rows of V^T
+#pragma unroll
+    for (int it = tid; it < 16 * (D / 8); it += kThreads) {
+      const int ng = it & 15, dg = it >> 4;
+      u32x4 rows[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t key = key0 + 4 * ng + i;
+        rows[i] = u32x4{0, 0, 0, 0};
+        if (key < a.Tk) rows[i] = *reinterpret_cast<const u32x4*>(vp + key * a.vs[2] + 8 * dg);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int sh = 16 * (e & 1);
+        const uint32_t x0 = (rows[0][e >> 1] >> sh) & 0xffffu, x1 = (rows[1][e >> 1] >> sh) & 0xffffu;
+        const uint32_t x2 = (rows[2][e >> 1] >> sh) & 0xffffu, x3 = (rows[3][e >> 1] >> sh) & 0xffffu;
+        *reinterpret_cast<u32x2*>(&vt_lds[(8 * dg + e) * VST + 4 * ng]) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
+      }
+    }
+    __syncthreads();
+
+    // S^T (keys x queries) for the two 32-key halves of the tile
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks) {
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * kb + l32) * KST + 16 * ks + 8 * h]);
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    // Lane (l32, h), register v of half kb holds key 32*kb + 8*(v/4) + 4*h + v%4
+    if ((MASK && cls == kTilePartial) || key0 + BN > a.kv_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+          bool vis = key < a.kv_end;
+          if (MASK && cls == kTilePartial && vis) vis = qvalid && mrow[key] != 0;
+          if (!vis) s[kb][v] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    const float mxc = wave_max_pair(mx) * a.c;
+    if (__ballot(mxc > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mxc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+    }
+    bf16x8 pf[2][2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], a.c, -m_run));
+        l_run += p;
+        pf[kb][v >> 3][v & 7] = static_cast<__bf16>(p);
+      }
+    }
+    // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
+    // of the half-tile kb; the V^T operand takes the same keys.
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+          const uint16_t* vrow = &vt_lds[(32 * d + l32) * VST + 32 * kb + 16 * j2 + 4 * h];
+          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
+          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
+          const u32x4 vv = u32x4{lo[0], lo[1], hi[0], hi[1]};
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kb][j2], oacc[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    uint16_t* orow = op + qrow * a.os[2];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        bf16x4 ov;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[d][4 * g + i] * inv);
+        *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g + 4 * h) = ov;
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- fp32 kernel
+
+// Same structure with v_mfma_f32_32x32x2f32: each k-step contracts two values,
+// one per lane half.  V needs no transpose (one element per lane per step).
+template <int D, bool MASK>
+__global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
+  static_assert(D % 16 == 0, "f32 path needs D divisible by 16");
+  constexpr int KST = D + 1;                 // odd stride: column reads hit distinct banks
+  constexpr int VST = D + 4;
+  constexpr int NDB = (D + 31) / 32;
+  __shared__ float k_lds[BN * KST];
+  __shared__ float v_lds[BN * VST];
+
+  const TileCoord tc = decode_tile<MASK>(a);
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, h = lane >> 5;
+
+  const float* qp = static_cast<const float*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
+  const float* kp = static_cast<const float*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
+  const float* vp = static_cast<const float*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
+  float* op = static_cast<float*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
+
+  const int64_t qrow = int64_t(tc.qt) * BM + w * 32 + l32;
+  const bool qvalid = qrow < a.Tq;
+  float qf[D / 2];
+#pragma unroll
+  for (int s = 0; s < D / 2; ++s) qf[s] = qvalid ? qp[qrow * a.qs[2] + 2 * s + h] : 0.f;
+
+  f32x16 oacc[NDB];
+#pragma unroll
+  for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
+  float m_run = -1e30f, l_run = 0.f;
+
+  const uint8_t* cls_row = nullptr;
+  const uint8_t* mrow = nullptr;
+  if (MASK) {
+    const int64_t bm = a.mask_bs ? tc.b : 0;
+    cls_row = a.cls + (bm * a.nqt + tc.qt) * int64_t(a.nkt);
+    mrow = a.mask + tc.b * a.mask_bs + qrow * a.Tk;
+  }
+
+  const int nkt_eff = int((a.kv_end + BN - 1) / BN);
+  for (int kt = 0; kt < nkt_eff; ++kt) {
+    uint8_t cls = kTileFull;
+    if (MASK) {
+      cls = cls_row[kt];
+      if (cls == kTileEmpty) continue;
+    }
+    const int64_t key0 = int64_t(kt) * BN;
+    __syncthreads();
+    for (int c = tid; c < BN * D / 4; c += kThreads) {
+      const int n = c / (D / 4), dc = c % (D / 4);
+      u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+      if (key0 + n < a.Tk) {
+        kv = *reinterpret_cast<const u32x4*>(kp + (key0 + n) * a.ks[2] + 4 * dc);
+        vv = *reinterpret_cast<const u32x4*>(vp + (key0 + n) * a.vs[2] + 4 * dc);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        k_lds[n * KST + 4 * dc + i] = __uint_as_float(kv[i]);
+        v_lds[n * VST + 4 * dc + i] = __uint_as_float(vv[i]);
+      }
+    }
+    __syncthreads();
+
+    f32x16 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x16{};
+#pragma unroll
+      for (int ks = 0; ks < D / 2; ++ks)
+        s[kb] = __builtin_amdgcn_mfma_f32_32x32x2f32(k_lds[(32 * kb + l32) * KST + 2 * ks + h], qf[ks], s[kb], 0, 0, 0);
+    }
+    if ((MASK && cls == kTilePartial) || key0 + BN > a.kv_end) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int64_t key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+          bool vis = key < a.kv_end;
+          if (MASK && cls == kTilePartial && vis) vis = qvalid && mrow[key] != 0;
+          if (!vis) s[kb][v] = -INFINITY;
+        }
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
+    const float mxc = wave_max_pair(mx) * a.c;
+    if (__ballot(mxc > m_run + kRescaleSlack) != 0) {
+      const float m_new = fmaxf(m_run, mxc);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+      l_run *= alpha;
+#pragma unroll
+      for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
+      m_run = m_new;
+    }
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], a.c, -m_run));
+        l_run += p;
+        s[kb][v] = p;
+      }
+    }
+    // O^T += V^T P^T, one key per lane half per step: step (kb, v) contracts key
+    // 32*kb + 8*(v/4) + 4*h + v%4 of lane half h.
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+      const int dim = 32 * d + l32;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          const int key = 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
+          const float vval = dim < D ? v_lds[key * VST + dim] : 0.f;
+          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x2f32(vval, s[kb][v], oacc[d], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+  if (qvalid) {
+    float* orow = op + qrow * a.os[2];
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int dim = 32 * d + 8 * g + 4 * h;
+        if (dim < D) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) orow[dim + i] = oacc[d][4 * g + i] * inv;
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- mask tiles
+
+// One workgroup per (batch, q-tile, k-tile): reads the tile's in-range mask
+// bytes once and records whether none, all, or some of them are set.
+__global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
+                                                               int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls) {
+  const int kt = blockIdx.x, qt = blockIdx.y;
+  const int64_t b = blockIdx.z;
+  const int64_t row = int64_t(qt) * BM + (threadIdx.x >> 1);
+  const int64_t col0 = int64_t(kt) * BN + 32 * (threadIdx.x & 1);
+  int any = 0, all = 1;
+  if (row < Tq) {
+    const uint8_t* p = mask + b * mask_bs + row * Tk;
+    for (int c = 0; c < 32; ++c) {
+      if (col0 + c < Tk) {
+        const int set = p[col0 + c] != 0;
+        any |= set;
+        all &= set;
+      }
+    }
+  }
+  any = __syncthreads_or(any);
+  all = __syncthreads_and(all);
+  if (threadIdx.x == 0) cls[(b * nqt + qt) * int64_t(nkt) + kt] = !any ? kTileEmpty : (all ? kTileFull : kTilePartial);
+}
+
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+bool nonneg(const sp_attn_strides& s) { return s.rank >= 0 && s.batch >= 0 && s.token >= 0 && s.head >= 0; }
+
+bool multiple_of(const sp_attn_strides& s, int64_t m) {
+  return s.rank % m == 0 && s.batch % m == 0 && s.token % m == 0 && s.head % m == 0;
+}
+
+// Byte extent [base, base + span) reached through a strided view.
+int64_t span_bytes(const sp_attn_strides& s, int64_t R, int64_t B, int64_t T, int64_t H, int64_t D, int64_t eb) {
+  return ((R - 1) * s.rank + (B - 1) * s.batch + (T - 1) * s.token + (H - 1) * s.head + D) * eb;
+}
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+  const char* x = static_cast<const char*>(a);
+  const char* y = static_cast<const char*>(b);
+  return x < y + nb && y < x + na;
+}
+
+template <int D, bool MASK>
+void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
+  if (dt == SP_BF16) {
+    if constexpr (D % 32 == 0) hipLaunchKernelGGL((attn_bf16_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
+  } else {
+    hipLaunchKernelGGL((attn_f32_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
+  }
+}
+
+template <bool MASK>
+sp_status dispatch_d(int D, const AttnArgs& a, sp_dtype dt, hipStream_t s) {
+  switch (D) {
+    case 16:
+      if (dt == SP_BF16) return SP_ERR_UNSUPPORTED;
+      launch_attn<16, MASK>(a, dt, s);
+      break;
+    case 64: launch_attn<64, MASK>(a, dt, s); break;
+    case 128: launch_attn<128, MASK>(a, dt, s); break;
+    default: return SP_ERR_UNSUPPORTED;
+  }
+  return launch_status();
+}
+
+}  // namespace
+}  // namespace sp
+
+using namespace sp;
+
+extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
+                                                     int32_t D, sp_dtype dtype, int32_t has_mask,
+                                                     int64_t mask_batch_stride) {
+  (void)R; (void)Hl; (void)D; (void)dtype;
+  if (!has_mask || B <= 0 || Tq <= 0 || Tk <= 0) return 0;
+  const int64_t bm = mask_batch_stride ? B : 1;
+  return size_t(bm * div_up(Tq, BM) * div_up(Tk, BN));
+}
+
+extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
+                                         const void* v, sp_attn_strides vs, void* o, sp_attn_strides os,
+                                         int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
+                                         sp_dtype dtype, int64_t kv_valid_len, const uint8_t* mask,
+                                         int64_t mask_batch_stride, float scale, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
+  if (R < 0 || B < 0 || Tq < 0 || Tk < 0 || Hl < 0 || kv_valid_len < 0 || mask_batch_stride < 0)
+    return SP_ERR_INVALID_ARG;
+  if (!(D == 16 || D == 64 || D == 128) || (dtype == SP_BF16 && D == 16)) return SP_ERR_UNSUPPORTED;
+  if (!std::isfinite(scale)) return SP_ERR_INVALID_ARG;
+  if (R == 0 || B == 0 || Tq == 0 || Hl == 0) return SP_OK;
+  if (!q || !k || !v || !o) return SP_ERR_INVALID_ARG;
+  if (!nonneg(qs) || !nonneg(ks) || !nonneg(vs) || !nonneg(os)) return SP_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t vec = 16 / eb;   // elements per 16-byte group
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return SP_ERR_INVALID_ARG;
+  if (!multiple_of(qs, vec) || !multiple_of(ks, vec) || !multiple_of(vs, vec) || !multiple_of(os, vec))
+    return SP_ERR_INVALID_ARG;
+  const int64_t tk1 = Tk > 0 ? Tk : 1;
+  const int64_t on = span_bytes(os, R, B, Tq, Hl, D, eb);
+  if (overlap(o, on, q, span_bytes(qs, R, B, Tq, Hl, D, eb)) || overlap(o, on, k, span_bytes(ks, R, B, tk1, Hl, D, eb)) ||
+      overlap(o, on, v, span_bytes(vs, R, B, tk1, Hl, D, eb)))
+    return SP_ERR_INVALID_ARG;
+  const int64_t nqt = div_up(Tq, BM), nkt = div_up(Tk, BN);
+  const int64_t nwg = nqt * Hl * B * R;
+  if (nwg >= (int64_t(1) << 31) || nkt >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  const bool has_mask = mask != nullptr && Tk > 0;
+  const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, has_mask, mask_batch_stride);
+  if (has_mask && (workspace == nullptr || workspace_bytes < need)) return SP_ERR_INVALID_ARG;
+  if (has_mask && B > 65535) return SP_ERR_UNSUPPORTED;
+
+  AttnArgs a;
+  a.q = q; a.k = k; a.v = v; a.o = o;
+  const sp_attn_strides* src[4] = {&qs, &ks, &vs, &os};
+  int64_t* dst[4] = {a.qs, a.ks, a.vs, a.os};
+  for (int i = 0; i < 4; ++i) {
+    dst[i][0] = src[i]->rank; dst[i][1] = src[i]->batch; dst[i][2] = src[i]->token; dst[i][3] = src[i]->head;
+  }
+  a.B = B; a.Tq = Tq; a.Tk = Tk; a.Hl = Hl;
+  a.kv_end = kv_valid_len < Tk ? kv_valid_len : Tk;
+  a.mask = mask; a.mask_bs = mask_batch_stride;
+  a.cls = static_cast<const uint8_t*>(workspace);
+  a.nqt = int32_t(nqt); a.nkt = int32_t(nkt);
+  a.c = scale * 1.4426950408889634f;
+  a.nwg = uint32_t(nwg);
+  hipStream_t s = as_stream(stream);
+  if (has_mask) {
+    const int64_t bm = mask_batch_stride ? B : 1;
+    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt), unsigned(bm)), dim3(kThreads), 0, s,
+                       mask, mask_batch_stride, Tq, Tk, int32_t(nqt), int32_t(nkt), static_cast<uint8_t*>(workspace));
+    if (launch_status() != SP_OK) return SP_ERR_HIP;
+    return dispatch_d<true>(D, a, dtype, s);
+  }
+  return dispatch_d<false>(D, a, dtype, s);
+}

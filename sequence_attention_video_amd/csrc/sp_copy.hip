@@ -1,0 +1,382 @@
+// Data-movement kernels of the sequence-parallel path: pad (with the user-mask
+// extension), the token<->head relayout of the virtual ranks, and
+// gather/unpad.  All three are HBM-bound byte moves: every thread moves 16-byte
+// vectors, a wave covers 1 KiB of contiguous destination per instruction, and
+// no value is ever converted, so results are bit-exact by construction.
+//
+// Sources: page "LTX-2 序列并行拆解：token 切分、all2all 换头与 runner 接入全链路",
+// section "token 切片、换头、gather 还原", steps 补齐 (pad), 换头 (head swap) and
+// 还原 (restore).
+
+#include "sp_internal.h"
+
+namespace sp {
+namespace {
+
+constexpr int kUnroll = 4;                        // 16-byte vectors per thread
+constexpr int64_t kChunk = int64_t(kThreads) * kUnroll;
+constexpr int kMaxWorld = 128;                     // ranks per gather_unpad launch
+constexpr int kMaxGridY = 65535;
+
+using vec16 = uint4;
+
+// ------------------------------------------------------------------ relayout
+
+struct RelayoutArgs {
+  const char* src[3];
+  char* dst[3];
+  int64_t B;
+  int64_t tok_rank_b, tok_batch_b, tok_row_b;   // token side (bytes)
+  int64_t head_rank_b, head_batch_b;            // head side (bytes)
+  int64_t run_b;                                 // Hl*D*eb: one head group of one token
+  int64_t seg_b;                                 // Ts*run_b: one source rank's rows on the head side
+  uint32_t V;                                    // 16-byte vectors per run
+  FastDiv fdV;
+  uint32_t n_per_seg;                            // Ts*V vectors per (tensor, r, b, s)
+  uint32_t chunks;                               // workgroups per segment
+  int to_heads;                                  // 1: token side -> head side
+};
+
+// blockIdx.x = (source-token rank s, chunk), blockIdx.y = (head-group rank r,
+// batch b), blockIdx.z = tensor.  On the head side the segment (r, b, s) is
+// one contiguous block of Ts runs; on the token side each run sits inside a
+// token row at offset r*run_b.  Flat vector f of the segment is token t = f/V,
+// vector f%V of the run.
+__global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
+  const uint32_t s = blockIdx.x / a.chunks;
+  const uint32_t chunk = blockIdx.x - s * a.chunks;
+  const int64_t r = blockIdx.y / a.B;
+  const int64_t b = blockIdx.y - r * a.B;
+  const int n = blockIdx.z;
+  const char* src = a.src[n];
+  char* dst = a.dst[n];
+  const int64_t tok_off = s * a.tok_rank_b + b * a.tok_batch_b + r * a.run_b;
+  const int64_t head_off = r * a.head_rank_b + b * a.head_batch_b + int64_t(s) * a.seg_b;
+
+  vec16 buf[kUnroll];
+  int64_t waddr[kUnroll];
+  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_seg) {
+      const uint32_t t = fdiv(f, a.fdV);
+      const uint32_t v = f - t * a.V;
+      const int64_t tok = tok_off + int64_t(t) * a.tok_row_b + int64_t(v) * 16;
+      const int64_t head = head_off + int64_t(f) * 16;
+      const int64_t raddr = a.to_heads ? tok : head;
+      waddr[u] = a.to_heads ? head : tok;
+      buf[u] = *reinterpret_cast<const vec16*>(src + raddr);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_seg) *reinterpret_cast<vec16*>(dst + waddr[u]) = buf[u];
+  }
+}
+
+// ------------------------------------------------------------------ pad
+
+struct PadArgs {
+  const char* x;
+  char* y;
+  int64_t x_batch_b, y_batch_b;
+  int64_t copy_vecs;     // T*C*eb/16: vectors copied from x per batch
+  int64_t start_vec;     // first vector written (copy_vecs when padding in place)
+  int64_t end_vec;       // T_pad*C*eb/16
+};
+
+// blockIdx.y = batch.  Vectors below copy_vecs come from x, the rest are zero.
+__global__ __launch_bounds__(kThreads) void pad_tokens_kernel(PadArgs a) {
+  const int64_t b = blockIdx.y;
+  const char* x = a.x + b * a.x_batch_b;
+  char* y = a.y + b * a.y_batch_b;
+  const int64_t f0 = a.start_vec + int64_t(blockIdx.x) * kChunk + threadIdx.x;
+  vec16 buf[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t f = f0 + u * kThreads;
+    buf[u] = make_uint4(0, 0, 0, 0);
+    if (f < a.copy_vecs) buf[u] = *reinterpret_cast<const vec16*>(x + f * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t f = f0 + u * kThreads;
+    if (f < a.end_vec) *reinterpret_cast<vec16*>(y + f * 16) = buf[u];
+  }
+}
+
+struct MaskPadArgs {
+  const uint8_t* in;   // (B, T, T)
+  uint8_t* out;        // (B, Tp, Tp)
+  int64_t T, Tp;
+  int64_t total;       // B*Tp*Tp
+};
+
+// Each thread writes 16 consecutive output bytes (flat order).  Output byte
+// (b, i, j): i < T and j < T -> in[b, i, j]; i >= T and j < T -> 1 (a pad query
+// row sees every real key); j >= T -> 0 (pad keys are hidden from every row).
+__global__ __launch_bounds__(kThreads) void pad_mask_kernel(MaskPadArgs a) {
+  const int64_t p0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16;
+  if (p0 >= a.total) return;
+  const int64_t plane = a.Tp * a.Tp;
+  int64_t b = p0 / plane;
+  int64_t rem = p0 - b * plane;
+  int64_t i = rem / a.Tp;
+  int64_t j = rem - i * a.Tp;
+  uint8_t v[16];
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    uint8_t val = 0;
+    if (p0 + e < a.total && j < a.T) {
+      val = i < a.T ? a.in[(b * a.T + i) * a.T + j] : uint8_t(1);
+    }
+    v[e] = val;
+    if (++j == a.Tp) {
+      j = 0;
+      if (++i == a.Tp) { i = 0; ++b; }
+    }
+  }
+  if (p0 + 16 <= a.total) {
+    uint4 w;
+    w.x = v[0] | (v[1] << 8) | (v[2] << 16) | (uint32_t(v[3]) << 24);
+    w.y = v[4] | (v[5] << 8) | (v[6] << 16) | (uint32_t(v[7]) << 24);
+    w.z = v[8] | (v[9] << 8) | (v[10] << 16) | (uint32_t(v[11]) << 24);
+    w.w = v[12] | (v[13] << 8) | (v[14] << 16) | (uint32_t(v[15]) << 24);
+    *reinterpret_cast<uint4*>(a.out + p0) = w;
+  } else {
+    for (int e = 0; p0 + e < a.total; ++e) a.out[p0 + e] = v[e];
+  }
+}
+
+// ------------------------------------------------------------------ gather/unpad
+
+struct GatherArgs {
+  const char* in;
+  char* out;
+  int64_t rank_b, batch_b;   // input strides (bytes)
+  int64_t row_b;             // C*eb
+  int64_t T;
+  int32_t W;
+  int64_t cum[kMaxWorld + 1];  // prefix sums of the kept counts
+};
+
+// blockIdx.y = (batch b, rank r).  Rank r's kept rows are one contiguous block
+// of its shard and land as one contiguous block of the output at row cum[r].
+__global__ __launch_bounds__(kThreads) void gather_unpad_kernel(GatherArgs a) {
+  const int64_t b = blockIdx.y / a.W;
+  const int r = int(blockIdx.y - b * a.W);
+  const int64_t first = a.cum[r];
+  int64_t kept = a.cum[r + 1] - first;
+  if (first + kept > a.T) kept = a.T - first;
+  if (kept <= 0) return;
+  const int64_t nvec = kept * a.row_b / 16;
+  const char* src = a.in + r * a.rank_b + b * a.batch_b;
+  char* dst = a.out + (b * a.T + first) * a.row_b;
+  const int64_t f0 = int64_t(blockIdx.x) * kChunk + threadIdx.x;
+  vec16 buf[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t f = f0 + u * kThreads;
+    if (f < nvec) buf[u] = *reinterpret_cast<const vec16*>(src + f * 16);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const int64_t f = f0 + u * kThreads;
+    if (f < nvec) *reinterpret_cast<vec16*>(dst + f * 16) = buf[u];
+  }
+}
+
+int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// The W*B blocks of `len` elements at r*rs + b*bs (r < W, b < B) are pairwise
+// disjoint if the layout is rank-major (bs >= len, rs >= (B-1)*bs + len) or
+// batch-major (rs >= len, bs >= (W-1)*rs + len).
+bool disjoint_blocks(int64_t rs, int64_t bs, int64_t W, int64_t B, int64_t len) {
+  if (rs < 0 || bs < 0) return false;
+  const bool ranks = W <= 1, batches = B <= 1;
+  const bool rank_major = (batches || bs >= len) && (ranks || rs >= (B - 1) * bs + len);
+  const bool batch_major = (ranks || rs >= len) && (batches || bs >= (W - 1) * rs + len);
+  return rank_major || batch_major;
+}
+
+}  // namespace
+}  // namespace sp
+
+using namespace sp;
+
+extern "C" sp_status sp_pad(const void* x, int64_t x_batch_stride, void* y, int64_t B, int64_t T,
+                            int64_t T_pad, int64_t C, sp_dtype dtype, const uint8_t* mask_in,
+                            uint8_t* mask_out, void* stream) {
+  if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
+  if (B < 0 || T < 0 || C < 0 || T_pad < T) return SP_ERR_INVALID_ARG;
+  if (x != nullptr && y == nullptr) return SP_ERR_INVALID_ARG;
+  if ((mask_in == nullptr) != (mask_out == nullptr)) return SP_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const bool tokens = y != nullptr;           // x may be null only when there are no rows to copy
+  if (tokens && x == nullptr && B > 0 && T > 0 && C > 0) return SP_ERR_INVALID_ARG;
+  const bool in_place = tokens && x == y;
+  if (tokens) {
+    if ((C * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+    if (x_batch_stride < T * C || x_batch_stride < 0) return SP_ERR_INVALID_ARG;
+    if (in_place && x_batch_stride != T_pad * C) return SP_ERR_INVALID_ARG;
+    if ((x != nullptr && !aligned16(x)) || !aligned16(y) || (x_batch_stride * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+    if (B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+    if (!in_place && x != nullptr) {
+      const char* xs = static_cast<const char*>(x);
+      const char* ys = static_cast<const char*>(y);
+      const char* xe = xs + ((B > 0 ? B - 1 : 0) * x_batch_stride + T * C) * eb;
+      const char* ye = ys + B * T_pad * C * eb;
+      if (B > 0 && T * C > 0 && xs < ye && ys < xe) return SP_ERR_INVALID_ARG;
+    }
+  }
+  if (mask_in != nullptr) {
+    const uint8_t* ie = mask_in + B * T * T;
+    const uint8_t* oe = mask_out + B * T_pad * T_pad;
+    if (B > 0 && T > 0 && mask_in < oe && mask_out < ie) return SP_ERR_INVALID_ARG;
+    if (!aligned16(mask_out)) return SP_ERR_INVALID_ARG;
+  }
+  hipStream_t s = as_stream(stream);
+  if (tokens && B > 0 && T_pad * C > 0) {
+    PadArgs a;
+    a.x = static_cast<const char*>(x);
+    a.y = static_cast<char*>(y);
+    a.x_batch_b = x_batch_stride * eb;
+    a.y_batch_b = T_pad * C * eb;
+    a.copy_vecs = x != nullptr ? T * C * eb / 16 : 0;
+    a.end_vec = T_pad * C * eb / 16;
+    a.start_vec = in_place ? a.copy_vecs : 0;
+    const int64_t n = a.end_vec - a.start_vec;
+    if (n > 0) {
+      dim3 grid(unsigned(div_up(n, kChunk)), unsigned(B));
+      hipLaunchKernelGGL(pad_tokens_kernel, grid, dim3(kThreads), 0, s, a);
+      if (launch_status() != SP_OK) return SP_ERR_HIP;
+    }
+  }
+  if (mask_in != nullptr && B > 0 && T_pad > 0) {
+    MaskPadArgs m;
+    m.in = mask_in;
+    m.out = mask_out;
+    m.T = T;
+    m.Tp = T_pad;
+    m.total = B * T_pad * T_pad;
+    const int64_t threads = div_up(m.total, 16);
+    hipLaunchKernelGGL(pad_mask_kernel, dim3(unsigned(div_up(threads, kThreads))), dim3(kThreads), 0, s, m);
+    if (launch_status() != SP_OK) return SP_ERR_HIP;
+  }
+  return SP_OK;
+}
+
+extern "C" sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                                       int64_t B, int64_t T_pad, int32_t H, int32_t D, sp_dtype dtype,
+                                       sp_dir dir, sp_shard_strides tok, sp_shard_strides head,
+                                       void* stream) {
+  if (!dtype_ok(dtype) || (dir != SP_TOKENS_TO_HEADS && dir != SP_HEADS_TO_TOKENS)) return SP_ERR_INVALID_ARG;
+  if (W < 1 || B < 0 || T_pad < 0 || H < 1 || D < 1) return SP_ERR_INVALID_ARG;
+  if (T_pad % W != 0) return SP_ERR_NOT_DIVISIBLE;
+  if (H % W != 0) return SP_ERR_INVALID_ARG;
+  if (n_tensors < 1 || n_tensors > 3 || src == nullptr || dst == nullptr) return SP_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t Hl = H / W, Ts = T_pad / W;
+  const int64_t run = Hl * D;              // elements per (token, head group)
+  if ((run * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  // the (rank, batch) blocks of each side must not overlap each other
+  if (!disjoint_blocks(tok.rank, tok.batch, W, B, Ts * H * D) ||
+      !disjoint_blocks(head.rank, head.batch, W, B, T_pad * run))
+    return SP_ERR_INVALID_ARG;
+  const int64_t tok_shard = B > 0 ? (B - 1) * tok.batch + Ts * H * D : 0;
+  const int64_t head_shard = B > 0 ? (B - 1) * head.batch + T_pad * run : 0;
+  if (((tok.rank | tok.batch | head.rank | head.batch) * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  const int64_t tok_span = (W - 1) * tok.rank + tok_shard;
+  const int64_t head_span = (W - 1) * head.rank + head_shard;
+  const int64_t s_span = (dir == SP_TOKENS_TO_HEADS ? tok_span : head_span) * eb;
+  const int64_t d_span = (dir == SP_TOKENS_TO_HEADS ? head_span : tok_span) * eb;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (src[i] == nullptr || dst[i] == nullptr || !aligned16(src[i]) || !aligned16(dst[i])) return SP_ERR_INVALID_ARG;
+  }
+  // no destination may overlap any source or another destination
+  for (int i = 0; i < n_tensors && B > 0 && Ts > 0; ++i) {
+    const char* d0 = static_cast<const char*>(dst[i]);
+    for (int j = 0; j < n_tensors; ++j) {
+      const char* s0 = static_cast<const char*>(src[j]);
+      if (s0 < d0 + d_span && d0 < s0 + s_span) return SP_ERR_INVALID_ARG;
+      const char* d1 = static_cast<const char*>(dst[j]);
+      if (j != i && d1 < d0 + d_span && d0 < d1 + d_span) return SP_ERR_INVALID_ARG;
+    }
+  }
+  if (B == 0 || Ts == 0) return SP_OK;
+  const int64_t V = run * eb / 16;
+  if (Ts * V >= (int64_t(1) << 32) - kChunk) return SP_ERR_UNSUPPORTED;
+  if (int64_t(W) * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  RelayoutArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);
+    a.dst[i] = static_cast<char*>(dst[i < n_tensors ? i : 0]);
+  }
+  a.B = B;
+  a.tok_rank_b = tok.rank * eb;
+  a.tok_batch_b = tok.batch * eb;
+  a.tok_row_b = int64_t(H) * D * eb;
+  a.head_rank_b = head.rank * eb;
+  a.head_batch_b = head.batch * eb;
+  a.run_b = run * eb;
+  a.seg_b = Ts * run * eb;
+  a.V = uint32_t(V);
+  a.fdV = make_fastdiv(uint32_t(V));
+  a.n_per_seg = uint32_t(Ts * V);
+  a.chunks = uint32_t(div_up(Ts * V, kChunk));
+  a.to_heads = dir == SP_TOKENS_TO_HEADS;
+  const int64_t gx = int64_t(a.chunks) * W;
+  if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  dim3 grid(unsigned(gx), unsigned(W * B), unsigned(n_tensors));
+  hipLaunchKernelGGL(relayout_kernel, grid, dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" sp_status sp_gather_unpad(const void* in, sp_shard_strides in_strides, void* out, int32_t W,
+                                     int64_t B, int64_t Ts, int64_t C, const int64_t* counts, int64_t T,
+                                     sp_dtype dtype, void* stream) {
+  if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
+  if (W < 1 || B < 0 || Ts < 0 || C < 0 || T < 0) return SP_ERR_INVALID_ARG;
+  if (W > kMaxWorld) return SP_ERR_UNSUPPORTED;
+  const int64_t eb = elem_bytes(dtype);
+  if ((C * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  GatherArgs a;
+  a.cum[0] = 0;
+  for (int r = 0; r < W; ++r) {
+    const int64_t c = counts ? counts[r] : Ts;
+    if (c < 0 || c > Ts) return SP_ERR_INVALID_ARG;
+    a.cum[r + 1] = a.cum[r] + c;
+  }
+  if (a.cum[W] < T) return SP_ERR_INVALID_ARG;
+  if (B == 0 || T == 0 || C == 0) return SP_OK;
+  if (in == nullptr || out == nullptr || !aligned16(in) || !aligned16(out)) return SP_ERR_INVALID_ARG;
+  if (!disjoint_blocks(in_strides.rank, in_strides.batch, W, B, Ts * C)) return SP_ERR_INVALID_ARG;
+  const int64_t shard = (B - 1) * in_strides.batch + Ts * C;
+  if (((in_strides.rank | in_strides.batch) * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  {
+    const char* i0 = static_cast<const char*>(in);
+    const char* o0 = static_cast<const char*>(out);
+    const int64_t ispan = ((W - 1) * in_strides.rank + shard) * eb;
+    const int64_t ospan = B * T * C * eb;
+    if (i0 < o0 + ospan && o0 < i0 + ispan) return SP_ERR_INVALID_ARG;
+  }
+  if (int64_t(W) * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  a.in = static_cast<const char*>(in);
+  a.out = static_cast<char*>(out);
+  a.rank_b = in_strides.rank * eb;
+  a.batch_b = in_strides.batch * eb;
+  a.row_b = C * eb;
+  a.T = T;
+  a.W = W;
+  int64_t max_vec = 0;
+  for (int r = 0; r < W; ++r) {
+    int64_t kept = a.cum[r + 1] - a.cum[r];
+    if (a.cum[r] + kept > T) kept = T - a.cum[r];
+    if (kept > 0 && kept * a.row_b / 16 > max_vec) max_vec = kept * a.row_b / 16;
+  }
+  dim3 grid(unsigned(div_up(max_vec, kChunk)), unsigned(W * B));
+  hipLaunchKernelGGL(gather_unpad_kernel, grid, dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}

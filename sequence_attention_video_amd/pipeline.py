@@ -1,0 +1,148 @@
+"""One step of the sequence-parallel attention path on one GPU, W virtual ranks.
+
+Calls the library's entry points in the order of page "LTX-2 序列并行拆解：token
+切分、all2all 换头与 runner 接入全链路", section "token 切片、换头、gather 还原":
+补齐 (sp_pad) -> 切分 (sp_partition) -> 换头 (sp_relayout_heads, then
+sp_masked_attention on every rank's local heads, then sp_relayout_heads back)
+-> 还原 (sp_gather_unpad).  This module only allocates buffers and passes
+pointers, sizes and strides; every byte of the path is produced by HIP kernels.
+
+Memory layout in HBM (elements, row-major):
+  inputs   q, k, v            (B, T, H, D)       self-attention
+           q                  (B, Tq, H, D)      cross-attention (never exchanged)
+  padded   q, k, v            (B, T_pad, H, D)   rank s's token shard = rows s*Ts..s*Ts+Ts-1
+  head side q, k, v, o        (W, B, T_pad, Hl, D)   rank r's local heads r*Hl..r*Hl+Hl-1
+  token side o                (W, B, Ts, H, D)   rank s's local output
+  output                      (B, T, H, D)
+  mask                        (B, T, T) uint8 -> extended (B, T_pad, T_pad)
+"""
+
+from __future__ import annotations
+
+import math
+
+import torch
+
+from . import binding as sp
+from .workloads import Workload
+
+TORCH_DTYPE = {"f32": torch.float32, "bf16": torch.bfloat16}
+
+
+def to_device(arr, dtype: str, device) -> torch.Tensor:
+    """Host array (float32, or uint16 bf16 patterns) -> device tensor of the same bytes."""
+    t = torch.from_numpy(arr)
+    if dtype == "bf16":
+        t = t.view(torch.bfloat16)
+    return t.to(device)
+
+
+class UlyssesStep:
+    """Buffers and launch sequence for one workload (all W ranks in each launch)."""
+
+    def __init__(self, wl: Workload, q, k, v, mask=None, device="cuda"):
+        self.wl = wl
+        B, H, D, W = wl.B, wl.H, wl.D, wl.W
+        T, Tp, Hl = wl.T, wl.T_pad, wl.Hl
+        self.Ts = Tp // W
+        dt = TORCH_DTYPE[wl.dtype]
+        e = lambda *s, d=dt: torch.empty(*s, dtype=d, device=device)
+        self.q, self.k, self.v, self.mask = q, k, v, mask
+        self.need_pad = Tp != T
+        if wl.cross:
+            self.kp, self.vp = (e(B, Tp, H, D), e(B, Tp, H, D)) if self.need_pad else (k, v)
+            self.kh, self.vh = e(W, B, Tp, Hl, D), e(W, B, Tp, Hl, D)
+            Tq = wl.Tq
+            self.Tsq = Tq // W
+            self.oh = e(W, B, Tq, Hl, D)
+            self.ot = e(W, B, self.Tsq, H, D)
+            self.out = e(B, Tq, H, D)
+        else:
+            if self.need_pad:
+                self.qp, self.kp, self.vp = e(B, Tp, H, D), e(B, Tp, H, D), e(B, Tp, H, D)
+            else:
+                self.qp, self.kp, self.vp = q, k, v
+            self.qh, self.kh, self.vh = (e(W, B, Tp, Hl, D) for _ in range(3))
+            self.oh = e(W, B, Tp, Hl, D)
+            self.ot = e(W, B, self.Ts, H, D)
+            self.out = e(B, T, H, D)
+        self.mask_ext = None
+        self.workspace = None
+        if mask is not None:
+            if self.need_pad:
+                self.mask_ext = torch.empty(mask.shape[0], Tp, Tp, dtype=torch.uint8, device=device)
+            else:
+                self.mask_ext = mask          # already (B, T_pad, T_pad): extension is the identity
+            need = sp.sp_masked_attention_workspace_size(W, B, Tp, Tp, Hl, D, sp._dtype_code(self.qh), True,
+                                                         Tp * Tp if mask.shape[0] > 1 else 0)
+            self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        self.scale = 1.0 / math.sqrt(D)
+
+    # -- the step's stages, each one library call (or one host call) ----------
+    def pad(self):
+        wl = self.wl
+        if not self.need_pad:
+            return
+        if wl.cross:
+            pairs = [(self.k, self.kp), (self.v, self.vp)]
+        else:
+            pairs = [(self.q, self.qp), (self.k, self.kp), (self.v, self.vp)]
+        for i, (x, y) in enumerate(pairs):
+            C = wl.H * wl.D
+            first = i == 0 and self.mask is not None
+            sp.sp_pad(x.view(wl.B, wl.T, C), y.view(wl.B, wl.T_pad, C), wl.T_pad,
+                      mask_in=self.mask if first else None, mask_out=self.mask_ext if first else None)
+
+    def partition(self):
+        return sp.sp_partition(self.wl.T_pad, self.wl.W)
+
+    def send_recv_heads(self):
+        wl = self.wl
+        tok = (self.Ts * wl.H * wl.D, wl.T_pad * wl.H * wl.D)   # rank shards are views of (B, T_pad, H, D)
+        if wl.cross:
+            src, dst = [self.kp, self.vp], [self.kh, self.vh]
+        else:
+            src, dst = [self.qp, self.kp, self.vp], [self.qh, self.kh, self.vh]
+        sp.sp_relayout_heads(src, dst, wl.W, wl.B, wl.T_pad, wl.H, wl.D, sp.SP_TOKENS_TO_HEADS, tok_strides=tok)
+
+    def attention(self):
+        wl = self.wl
+        B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
+        head_side = (B * Tp * Hl * D, Tp * Hl * D, Hl * D, D)
+        if wl.cross:
+            Tq = wl.Tq
+            qs = (Hl * D, Tq * H * D, H * D, D)            # rank r's heads of the unexchanged Q
+            os_ = (B * Tq * Hl * D, Tq * Hl * D, Hl * D, D)
+            sp.sp_masked_attention(self.q, self.kh, self.vh, self.oh, wl.W, B, Tq, Tp, Hl, D,
+                                   qs, head_side, head_side, os_, kv_valid_len=wl.T, scale=self.scale)
+            return
+        if self.mask is not None:
+            sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, Tp, Tp, Hl, D,
+                                   head_side, head_side, head_side, head_side, kv_valid_len=Tp,
+                                   mask=self.mask_ext, scale=self.scale, workspace=self.workspace)
+        else:
+            sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, Tp, Tp, Hl, D,
+                                   head_side, head_side, head_side, head_side, kv_valid_len=wl.T,
+                                   scale=self.scale)
+
+    def gather_heads(self):
+        wl = self.wl
+        Tq_pad = wl.Tq if wl.cross else wl.T_pad
+        sp.sp_relayout_heads([self.oh], [self.ot], wl.W, wl.B, Tq_pad, wl.H, wl.D, sp.SP_HEADS_TO_TOKENS)
+
+    def gather_output_tokens(self, lengths):
+        wl = self.wl
+        C = wl.H * wl.D
+        if wl.cross:
+            sp.sp_gather_unpad(self.ot, self.out, wl.W, wl.B, self.Tsq, C, wl.Tq, counts=[self.Tsq] * wl.W)
+        else:
+            sp.sp_gather_unpad(self.ot, self.out, wl.W, wl.B, self.Ts, C, wl.T, counts=lengths)
+
+    def run(self):
+        self.pad()
+        _, lengths = self.partition()
+        self.send_recv_heads()
+        self.attention()
+        self.gather_heads()
+        self.gather_output_tokens(lengths)
+        return self.out

@@ -1,0 +1,157 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+include/sp.h declares, and its host-only logic (partition, status names,
+argument validation that returns before anything is launched) behaves as the
+header says."""
+
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from tests.conftest import ROOT, load_golden
+
+HEADER = os.path.join(ROOT, "include", "sp.h")
+LIB = os.path.join(ROOT, "sequence_attention_video_amd", "libspattn.so")
+
+
+def declared_functions():
+    text = open(HEADER, encoding="utf-8").read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sp_[a-z_0-9]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail("libspattn.so is not built (run __graft_entry__.build())")
+    from sequence_attention_video_amd import binding
+    return binding.load()
+
+
+def test_header_declares_the_five_calls():
+    names = declared_functions()
+    for n in ("sp_pad", "sp_partition", "sp_relayout_heads", "sp_masked_attention", "sp_gather_unpad"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", LIB], capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (sp_[a-z_0-9]+)$", out, flags=re.M))
+    missing = [n for n in declared_functions() if n not in exported]
+    assert not missing, missing
+    from sequence_attention_video_amd import binding
+    assert sorted(binding.EXPORTS) == declared_functions()
+
+
+def test_partition_through_the_abi(lib):
+    from sequence_attention_video_amd import binding
+    g = load_golden("partition.txt")
+    for case in g["cases"]:
+        if case[2] == "ValueError":
+            with pytest.raises(ValueError):
+                binding.sp_partition(case[0], case[1])
+        else:
+            assert binding.sp_partition(case[0], case[1]) == (case[2], case[3])
+    with pytest.raises(ValueError):
+        binding.sp_partition(8, 0)
+    assert lib.sp_partition(52, 4, None, None) == binding.SP_OK
+    assert lib.sp_partition(50, 4, None, None) == binding.SP_ERR_NOT_DIVISIBLE
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.sp_status_string(s).startswith(b"SP_")
+    assert lib.sp_status_string(99) == b"SP_ERR_UNKNOWN"
+    assert lib.sp_version() >= 100
+
+
+def test_validation_returns_before_launch(lib):
+    """Invalid requests are refused on the host; nothing is launched (null
+    pointers would fault if anything were)."""
+    from sequence_attention_video_amd import binding as b
+    S, A = b.ShardStrides, b.AttnStrides
+    nul = (ctypes.c_void_p * 3)(None, None, None)
+    # relayout: T_pad not divisible by W -> NOT_DIVISIBLE (checked before pointers)
+    assert lib.sp_relayout_heads(nul, nul, 3, 8, 1, 6150, 32, 128, b.SP_BF16, b.SP_TOKENS_TO_HEADS,
+                                 S(0, 0), S(0, 0), None) == b.SP_ERR_NOT_DIVISIBLE
+    # H not divisible by W
+    assert lib.sp_relayout_heads(nul, nul, 3, 8, 1, 6152, 30, 128, b.SP_BF16, b.SP_TOKENS_TO_HEADS,
+                                 S(0, 0), S(0, 0), None) == b.SP_ERR_INVALID_ARG
+    # null tensors
+    assert lib.sp_relayout_heads(nul, nul, 3, 8, 1, 6152, 32, 128, b.SP_BF16, b.SP_TOKENS_TO_HEADS,
+                                 S(0, 0), S(0, 0), None) == b.SP_ERR_INVALID_ARG
+    # n_tensors out of range
+    assert lib.sp_relayout_heads(nul, nul, 4, 8, 1, 6152, 32, 128, b.SP_BF16, b.SP_TOKENS_TO_HEADS,
+                                 S(0, 0), S(0, 0), None) == b.SP_ERR_INVALID_ARG
+    # pad: T_pad < T, unpaired pointers
+    assert lib.sp_pad(None, 0, None, 1, 10, 8, 64, b.SP_BF16, None, None, None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_pad(ctypes.c_void_p(16), 640, None, 1, 10, 12, 64, b.SP_BF16, None, None, None) == b.SP_ERR_INVALID_ARG
+    # attention: unsupported head dim, negative kv_valid_len, missing workspace for a mask
+    z = A(0, 0, 0, 0)
+    assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 96, b.SP_BF16, 64,
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+    assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 16, b.SP_BF16, 64,
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+    assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 128, b.SP_BF16, -1,
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 128, b.SP_BF16, 64,
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
+    # empty problems are a no-op success
+    assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 0, 64, 1, 128, b.SP_BF16, 64,
+                                   None, 0, 0.1, None, 0, None) == b.SP_OK
+    # gather: counts inconsistent with T, count above Ts
+    c = (ctypes.c_int64 * 2)(3, 2)
+    assert lib.sp_gather_unpad(None, S(0, 0), None, 2, 1, 3, 64, c, 6, b.SP_BF16, None) == b.SP_ERR_INVALID_ARG
+    c = (ctypes.c_int64 * 2)(4, 2)
+    assert lib.sp_gather_unpad(None, S(0, 0), None, 2, 1, 3, 64, c, 5, b.SP_BF16, None) == b.SP_ERR_INVALID_ARG
+
+
+def test_workspace_size(lib):
+    from sequence_attention_video_amd import binding as b
+    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == 0
+    # one byte per (128-row, 64-key) tile of the mask
+    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == 49 * 97
+    assert b.sp_masked_attention_workspace_size(1, 2, 256, 128, 4, 64, b.SP_BF16, True, 256 * 128) == 2 * 2 * 2
+
+
+def test_fast_division_host_twin(tmp_path):
+    """The multiply-high division used by the relayout kernel, exhaustively on
+    small values and on sampled large ones, against plain integer division."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    src = tmp_path / "fd.cpp"
+    src.write_text(r"""
+#include "sp_fastdiv.h"
+#include <cstdio>
+#include <cstdint>
+#include <initializer_list>
+int main() {
+  uint64_t bad = 0, x = 88172645463325252ull;
+  for (uint32_t d = 1; d < 2000; ++d) {
+    sp::FastDiv f = sp::make_fastdiv(d);
+    for (uint32_t n = 0; n < 5000; ++n) bad += sp::fdiv_host(n, f) != n / d;
+    for (int i = 0; i < 2000; ++i) {
+      x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+      uint32_t n = uint32_t(x);
+      bad += sp::fdiv_host(n, f) != n / d;
+    }
+    bad += sp::fdiv_host(0xffffffffu, f) != 0xffffffffu / d;
+  }
+  const uint32_t big[] = {65536u, 65537u, 1u << 31, (1u << 31) + 1, 0xfffffffeu, 0xffffffffu, 3000000019u};
+  for (uint32_t d : big) {
+    sp::FastDiv f = sp::make_fastdiv(d);
+    for (uint32_t n : {0u, 1u, d - 1, d, d + 1, 0xffffffffu, 0x80000000u}) bad += sp::fdiv_host(n, f) != n / d;
+  }
+  printf("%llu\n", (unsigned long long)bad);
+  return bad != 0;
+}
+""")
+    exe = tmp_path / "fd"
+    subprocess.run([gxx, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "sequence_attention_video_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0 and res.stdout.strip() == "0", res.stdout
