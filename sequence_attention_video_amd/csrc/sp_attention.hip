@@ -8,20 +8,27 @@
 // keys visible).
 //
 // Design (bf16):
-//   * one workgroup = 4 waves = 128 query rows of one (rank, batch, head); each
-//     wave owns 32 query rows for the whole key loop;
-//   * key tiles of 64 are staged in LDS: K row-major, V transposed (V^T), both
-//     padded so the MFMA operand reads are bank-conflict free;
+//   * one workgroup = 4 waves = 256 query rows of one (rank, batch, head), one
+//     wave per SIMD; each wave owns 64 query rows (two 32-row blocks) for the
+//     whole key loop, so every K or V operand read from LDS feeds two MFMAs
+//     (LDS reads run at about half of the LDS bandwidth at MFMA peak);
+//   * key tiles of 64 are fetched with 16-byte direct global->LDS loads into a
+//     double buffer, one barrier per tile; the chunk order inside each row is
+//     XOR-swizzled so that the MFMA operand reads are bank-conflict free;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
 //     operand).  In the 32x32 accumulator layout a lane holds 16 keys of ONE
 //     query, so the row max/sum are in-lane plus one swap with lane^32, and the
 //     same registers, rounded to bf16, are directly the B operand of
-//     O^T += V^T P^T (second MFMA), whose accumulator again gives each lane one
-//     query: the softmax rescale is a per-lane scalar;
+//     O^T += V^T P^T, whose accumulator again gives each lane one query: the
+//     softmax rescale is a per-lane scalar.  The V^T operand is read from the
+//     row-major V tile with the LDS transpose read ds_read_b64_tr_b16;
 //   * softmax in float32 with exp2 (scale*log2 e folded into one FMA); the
 //     running max is only raised when a tile's max exceeds it by more than 2^8,
 //     so the O rescale runs rarely while p stays <= 256 (exact in float32,
-//     representable in bf16);
+//     representable in bf16); row sums add the bf16-rounded p with v_dot2;
+//   * the two query blocks are software-pipelined inside the wave: the QK^T
+//     MFMAs of block 1 run under the exponentials of block 0, and the PV MFMAs
+//     of block 0 under the exponentials of block 1;
 //   * user masks are classified once per call into empty/full/partial tiles:
 //     empty tiles are skipped, full tiles read no mask bytes;
 //   * workgroup ids are remapped so that the 8 XCDs each take a contiguous run
@@ -35,8 +42,9 @@
 namespace sp {
 namespace {
 
-constexpr int BM = 128;              // query rows per workgroup
-constexpr int BN = 64;               // keys per tile
+constexpr int BM = 256;              // query rows per bf16 workgroup, and the mask-class tile height
+constexpr int BM32 = 128;            // query rows per fp32 workgroup
+constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
@@ -46,6 +54,10 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct AttnArgs {
   const void* q;
@@ -58,8 +70,9 @@ struct AttnArgs {
   int64_t kv_end;                        // keys >= kv_end are never visible
   const uint8_t* mask;                   // (B, Tq, Tk) or null
   int64_t mask_bs;                       // batch stride of mask (0 = shared)
-  const uint8_t* cls;                    // tile classes (Bm, nqt, nkt)
-  int32_t nqt, nkt;
+  const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt), BM x BN tiles
+  int32_t nqt, nkt;                      // query tiles of this kernel, key tiles of BN
+  int32_t nqt_cls;                       // query tiles of the class map (height BM)
   float c;                               // scale * log2(e)
   uint32_t nwg;
 };
@@ -99,15 +112,50 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 
 // ---------------------------------------------------------------- bf16 kernel
 
+// Waits until this wave's direct global->LDS loads have landed (vmcnt = 0; the
+// expcnt and lgkmcnt fields are left at their maximum, i.e. not waited on).
+__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS layout of one K or V tile (BN keys x D dims, bf16).  The tile is cut
+// into groups of KPG keys whose rows make exactly 1 KiB (KPG = 4 at D = 128,
+// 8 at D = 64); one 16-byte direct load of a wave (64 lanes) fills one group,
+// reading KPG whole rows.  Groups sit GROUP_BYTES apart (1 KiB + 64 B of
+// padding, which shifts consecutive groups by 16 banks).  Inside a group,
+// chunk c (dims 8c .. 8c+7) of key n sits at c*KPG*16 + pos*16 with pos the
+// key's index in the group, XOR 4 on odd chunks when KPG = 8.  With this
+// layout the 8 lanes of each ds_read_b128 phase (8 keys, one chunk) and the
+// 16 lanes of each transpose read (4 keys x 2 adjacent chunks) touch 32
+// different banks, and every read address is a per-lane base plus a
+// compile-time offset.
+template <int D>
+struct Bf16Tile {
+  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
+  static constexpr int KPG = 512 / D;               // keys per 1 KiB group
+  static constexpr int NG = BN / KPG;               // groups per tile = direct loads per tile
+  static constexpr int NLD = NG / 4;                // direct loads per wave per tile and tensor
+  static constexpr int GROUP_BYTES = 1024 + 64;
+  static constexpr int TILE_BYTES = NG * GROUP_BYTES;
+  static constexpr int NKS = D / 16;                // k-steps of QK^T
+  static constexpr int NDB = D / 32;                // 32-row blocks of O^T
+  static_assert(D == 64 || D == 128, "bf16 tiles are built for D = 64 and 128");
+
+  static __host__ __device__ constexpr int pos(int n, int c) {
+    return KPG == 8 ? ((n % KPG) ^ (4 * (c & 1))) : (n % KPG);
+  }
+  // byte offset of chunk c of key n inside the tile
+  static __host__ __device__ constexpr int offset(int n, int c) {
+    return (n / KPG) * GROUP_BYTES + c * KPG * 16 + pos(n, c) * 16;
+  }
+};
+
 template <int D, bool MASK>
 __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
-  static_assert(D % 32 == 0, "bf16 path needs D divisible by 32");
-  constexpr int KST = D + 8;     // K tile row stride (elements)
-  constexpr int VST = BN + 4;    // V^T tile row stride (elements)
-  constexpr int NKS = D / 16;    // k-steps of the QK^T MFMA
-  constexpr int NDB = D / 32;    // 32-row blocks of O^T
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[BN * KST];
-  __shared__ __attribute__((aligned(16))) uint16_t vt_lds[D * VST];
+  using T = Bf16Tile<D>;
+  constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD;
+  __shared__ __attribute__((aligned(1024))) char k_lds0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char v_lds1[T::TILE_BYTES];
 
   const TileCoord tc = decode_tile<MASK>(a);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -118,147 +166,219 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
   uint16_t* op = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
 
-  const int64_t qrow = int64_t(tc.qt) * BM + w * 32 + l32;
-  const bool qvalid = qrow < a.Tq;
-
-  bf16x8 qf[NKS];
+  // query rows of this lane: block qb covers rows 64*w + 32*qb .. +31 of the tile
+  int64_t qrow[2];
+  bool qvalid[2];
+  bf16x8 qf[2][NKS];
 #pragma unroll
-  for (int s = 0; s < NKS; ++s) {
-    qf[s] = bf16x8{};
-    if (qvalid) qf[s] = *reinterpret_cast<const bf16x8*>(qp + qrow * a.qs[2] + 16 * s + 8 * h);
+  for (int qb = 0; qb < 2; ++qb) {
+    qrow[qb] = int64_t(tc.qt) * BM + 64 * w + 32 * qb + l32;
+    qvalid[qb] = qrow[qb] < a.Tq;
+#pragma unroll
+    for (int s = 0; s < NKS; ++s) {
+      qf[qb][s] = bf16x8{};
+      if (qvalid[qb]) qf[qb][s] = *reinterpret_cast<const bf16x8*>(qp + qrow[qb] * a.qs[2] + 16 * s + 8 * h);
+    }
   }
 
-  f32x16 oacc[NDB];
+  f32x16 oacc[2][NDB];
 #pragma unroll
-  for (int d = 0; d < NDB; ++d) oacc[d] = f32x16{};
-  float m_run = -1e30f;   // running max, log2 units (scaled score)
-  float l_run = 0.f;      // this lane's share of the softmax denominator
+  for (int qb = 0; qb < 2; ++qb)
+#pragma unroll
+    for (int d = 0; d < NDB; ++d) oacc[qb][d] = f32x16{};
+  float m_run[2] = {-1e30f, -1e30f};   // running max per query, log2 units
+  float l_run[2] = {0.f, 0.f};         // this lane's share of each denominator
 
   const uint8_t* cls_row = nullptr;
-  const uint8_t* mrow = nullptr;
+  const uint8_t* mrow[2] = {nullptr, nullptr};
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
-    cls_row = a.cls + (bm * a.nqt + tc.qt) * int64_t(a.nkt);
-    mrow = a.mask + tc.b * a.mask_bs + qrow * a.Tk;
+    cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) mrow[qb] = a.mask + tc.b * a.mask_bs + qrow[qb] * a.Tk;
   }
-
   const int nkt_eff = int((a.kv_end + BN - 1) / BN);
-  for (int kt = 0; kt < nkt_eff; ++kt) {
-    uint8_t cls = kTileFull;
-    if (MASK) {
-      cls = cls_row[kt];
-      if (cls == kTileEmpty) continue;
-    }
-    const int64_t key0 = int64_t(kt) * BN;
-    __syncthreads();   // every wave is done with the previous tile
-    // K tile, row-major
-#pragma unroll
-    for (int c = tid; c < BN * D / 8; c += kThreads) {
-      const int n = c / (D / 8), dc = c % (D / 8);
-      u32x4 val = u32x4{0, 0, 0, 0};
-      if (key0 + n < a.Tk) val = *reinterpret_cast<const u32x4*>(kp + (key0 + n) * a.ks[2] + 8 * dc);
-      *reinterpret_cast<u32x4*>(&k_lds[n * KST + 8 * dc]) = val;
-    }
-    // V tile, transposed: thread takes 4 keys x 8 dims and writes 8 rows of V^T
-#pragma unroll
-    for (int it = tid; it < 16 * (D / 8); it += kThreads) {
-      const int ng = it & 15, dg = it >> 4;
-      u32x4 rows[4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t key = key0 + 4 * ng + i;
-        rows[i] = u32x4{0, 0, 0, 0};
-        if (key < a.Tk) rows[i] = *reinterpret_cast<const u32x4*>(vp + key * a.vs[2] + 8 * dg);
-      }
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int sh = 16 * (e & 1);
-        const uint32_t x0 = (rows[0][e >> 1] >> sh) & 0xffffu, x1 = (rows[1][e >> 1] >> sh) & 0xffffu;
-        const uint32_t x2 = (rows[2][e >> 1] >> sh) & 0xffffu, x3 = (rows[3][e >> 1] >> sh) & 0xffffu;
-        *reinterpret_cast<u32x2*>(&vt_lds[(8 * dg + e) * VST + 4 * ng]) = u32x2{x0 | (x1 << 16), x2 | (x3 << 16)};
-      }
-    }
-    __syncthreads();
+  auto next_tile = [&](int kt) {
+    ++kt;
+    if (MASK)
+      while (kt < nkt_eff && cls_row[kt] == kTileEmpty) ++kt;
+    return kt;
+  };
 
-    // S^T (keys x queries) for the two 32-key halves of the tile
-    f32x16 s[2];
+  // Direct loads: per tile and tensor, wave w fills groups w*NLD .. w*NLD+NLD-1.
+  // Lane i of a load writes LDS byte 16*i of its group, which holds chunk
+  // c = i / KPG of the key whose pos() is i % KPG.  Keys past kv_end read row
+  // kv_end-1 instead (in bounds and finite); their scores are masked to -inf,
+  // so their weight is exactly 0.
+  const int ld_c = lane / KPG;
+  const int ld_n = (KPG == 8 ? ((lane % KPG) ^ (4 * (ld_c & 1))) : (lane % KPG));
+  const int wu = __builtin_amdgcn_readfirstlane(w);          // wave index, as a scalar
+  const int64_t k_lane = int64_t(ld_n) * a.ks[2] + 8 * ld_c;
+  const int64_t v_lane = int64_t(ld_n) * a.vs[2] + 8 * ld_c;
+  auto issue = [&](int kt, char* kdst, char* vdst) {
+    const int64_t key0 = int64_t(kt) * BN;
+    if (key0 + BN <= a.kv_end) {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int grp = wu * NLD + j;
+        const int64_t row = key0 + grp * KPG;
+        __builtin_amdgcn_global_load_lds(kp + row * a.ks[2] + k_lane, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + row * a.vs[2] + v_lane, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, 0, 0);
+      }
+    } else {
+#pragma unroll
+      for (int j = 0; j < NLD; ++j) {
+        const int grp = wu * NLD + j;
+        int64_t key = key0 + grp * KPG + ld_n;
+        if (key >= a.kv_end) key = a.kv_end - 1;
+        __builtin_amdgcn_global_load_lds(kp + key * a.ks[2] + 8 * ld_c, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(vp + key * a.vs[2] + 8 * ld_c, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, 0, 0);
+      }
+    }
+  };
+
+  // per-lane LDS bases: K fragment (key l32, chunk h); V transpose source
+  // (key 4*h + s16/4, chunk 2*dh + (s16%4)/2, byte 8*(s16%2))
+  const int g = lane >> 4, s16 = lane & 15, dh = g & 1;
+  const int k_base = T::offset(l32, h);
+  const int v_base = T::offset(4 * h + (s16 >> 2), 2 * dh + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
+
+  // One key tile on LDS buffers (kb_, vb_).
+  auto compute = [&](int kt, const char* kb_, const char* vb_) {
+    const int64_t key0 = int64_t(kt) * BN;
+    const uint8_t cls = MASK ? cls_row[kt] : uint8_t(kTileFull);
+    // S^T for both query blocks (keys x queries).  The K fragment (rows
+    // 32*kb + l32, chunk 2*ks + h) feeds both blocks.  Lane (l32, h), register v
+    // of half kb then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
+    f32x16 s[2][2];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[kb] = f32x16{};
+      s[0][kb] = f32x16{};
+      s[1][kb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[(32 * kb + l32) * KST + 16 * ks + 8 * h]);
-        s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+        // offset(32*kb + l32, 2*ks + h) - offset(l32, h) is lane-independent
+        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
+            kb_ + k_base + (T::offset(32 * kb, 2 * ks) - T::offset(0, 0)));
+        s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
+        s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
       }
     }
-    // Lane (l32, h), register v of half kb holds key 32*kb + 8*(v/4) + 4*h + v%4
     if ((MASK && cls == kTilePartial) || key0 + BN > a.kv_end) {
+      // register v of half kb is key key0 + 4*h + kofs(kb, v)
+      const int room = int(a.kv_end - key0) - 4 * h;   // visible iff kofs < room
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int qb = 0; qb < 2; ++qb) {
+        const uint8_t* mk = MASK ? mrow[qb] + key0 + 4 * h : nullptr;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = key0 + 32 * kb + 8 * (v >> 2) + 4 * h + (v & 3);
-          bool vis = key < a.kv_end;
-          if (MASK && cls == kTilePartial && vis) vis = qvalid && mrow[key] != 0;
-          if (!vis) s[kb][v] = -INFINITY;
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kofs = 32 * kb + 8 * (v >> 2) + (v & 3);
+            bool vis = kofs < room;
+            if (MASK && cls == kTilePartial && vis) vis = qvalid[qb] && mk[kofs] != 0;
+            if (!vis) s[qb][kb][v] = -INFINITY;
+          }
+      }
+    }
+    // softmax numerators, rounded to bf16: the B operands of the PV MFMA
+    bf16x8 pf[2][2][2];
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) {
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
+      const float mxc = wave_max_pair(mx) * a.c;
+      if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
+        const float m_new = fmaxf(m_run[qb], mxc);
+        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+        l_run[qb] *= alpha;
+#pragma unroll
+        for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
+        m_run[qb] = m_new;
+      }
+      const float nm = -m_run[qb];
+      float part[2] = {0.f, 0.f};
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            pf[qb][kb][j2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * j2 + e], a.c, nm)));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pair = {pf[qb][kb][j2][e], pf[qb][kb][j2][e + 1]};
+            part[j2] = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part[j2], false);
+          }
         }
-      }
-    }
-    float mx = -INFINITY;
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb][v]);
-    const float mxc = wave_max_pair(mx) * a.c;
-    if (__ballot(mxc > m_run + kRescaleSlack) != 0) {
-      const float m_new = fmaxf(m_run, mxc);
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int d = 0; d < NDB; ++d) oacc[d] *= alpha;
-      m_run = m_new;
-    }
-    bf16x8 pf[2][2];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const float p = __builtin_amdgcn_exp2f(__builtin_fmaf(s[kb][v], a.c, -m_run));
-        l_run += p;
-        pf[kb][v >> 3][v & 7] = static_cast<__bf16>(p);
-      }
+      l_run[qb] += part[0] + part[1];
     }
     // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
-    // of the half-tile kb; the V^T operand takes the same keys.
+    // of half-tile kb.  The V^T operand takes the same keys through two transpose
+    // reads: in each 16-lane group, source lane s addresses key k0 + s/4 at dims
+    // n0 + 4*(s%4) .. +3, and lane j receives dim n0 + j of keys k0 .. k0+3
+    // (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
+      for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
-          const uint16_t* vrow = &vt_lds[(32 * d + l32) * VST + 32 * kb + 16 * j2 + 4 * h];
-          const u32x2 lo = *reinterpret_cast<const u32x2*>(vrow);
-          const u32x2 hi = *reinterpret_cast<const u32x2*>(vrow + 8);
-          const u32x4 vv = u32x4{lo[0], lo[1], hi[0], hi[1]};
-          oacc[d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, vv), pf[kb][j2], oacc[d], 0, 0, 0);
+          constexpr int z = T::offset(0, 0);
+          const int o0 = T::offset(32 * kb + 16 * j2, 4 * d) - z;
+          const int o1 = T::offset(32 * kb + 16 * j2 + 8, 4 * d) - z;
+          const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + v_base + o0));
+          const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + v_base + o1));
+          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+#pragma unroll
+          for (int qb = 0; qb < 2; ++qb)
+            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][j2], oacc[qb][d], 0, 0, 0);
         }
-      }
     }
+  };
+
+  // Double-buffered tile loop, unrolled by two so that each LDS buffer is a
+  // distinct object: loads of the next tile overlap the compute of this one,
+  // and one barrier per tile separates the buffer reuse.
+  int kt = MASK ? next_tile(-1) : 0;
+  if (kt < nkt_eff) issue(kt, k_lds0, v_lds0);
+  wait_vmem();
+  __syncthreads();
+  while (kt < nkt_eff) {
+    int kn = next_tile(kt);
+    if (kn < nkt_eff) issue(kn, k_lds1, v_lds1);
+    compute(kt, k_lds0, v_lds0);
+    wait_vmem();
+    __syncthreads();
+    kt = kn;
+    if (kt >= nkt_eff) break;
+    kn = next_tile(kt);
+    if (kn < nkt_eff) issue(kn, k_lds0, v_lds0);
+    compute(kt, k_lds1, v_lds1);
+    wait_vmem();
+    __syncthreads();
+    kt = kn;
   }
 
   // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4
-  const float lt = l_run + __shfl_xor(l_run, 32);
-  const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-  if (qvalid) {
-    uint16_t* orow = op + qrow * a.os[2];
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
+  for (int qb = 0; qb < 2; ++qb) {
+    const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
+    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+    if (qvalid[qb]) {
+      uint16_t* orow = op + qrow[qb] * a.os[2];
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        bf16x4 ov;
+      for (int d = 0; d < NDB; ++d) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[d][4 * g + i] * inv);
-        *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g + 4 * h) = ov;
+        for (int g4 = 0; g4 < 4; ++g4) {
+          bf16x4 ov;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[qb][d][4 * g4 + i] * inv);
+          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * h) = ov;
+        }
       }
     }
   }
@@ -286,7 +406,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const float* vp = static_cast<const float*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
   float* op = static_cast<float*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
 
-  const int64_t qrow = int64_t(tc.qt) * BM + w * 32 + l32;
+  const int64_t qrow = int64_t(tc.qt) * BM32 + w * 32 + l32;
   const bool qvalid = qrow < a.Tq;
   float qf[D / 2];
 #pragma unroll
@@ -301,7 +421,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const uint8_t* mrow = nullptr;
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
-    cls_row = a.cls + (bm * a.nqt + tc.qt) * int64_t(a.nkt);
+    // a class tile is BM rows high: it holds this workgroup's BM32 rows
+    cls_row = a.cls + (bm * a.nqt_cls + tc.qt * BM32 / BM) * int64_t(a.nkt);
     mrow = a.mask + tc.b * a.mask_bs + qrow * a.Tk;
   }
 
@@ -413,14 +534,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 // bytes once and records whether none, all, or some of them are set.
 __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
                                                                int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls) {
+  static_assert(BM == kThreads, "one mask row per thread");
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int64_t row = int64_t(qt) * BM + (threadIdx.x >> 1);
-  const int64_t col0 = int64_t(kt) * BN + 32 * (threadIdx.x & 1);
+  const int64_t row = int64_t(qt) * BM + threadIdx.x;
+  const int64_t col0 = int64_t(kt) * BN;
   int any = 0, all = 1;
   if (row < Tq) {
     const uint8_t* p = mask + b * mask_bs + row * Tk;
-    for (int c = 0; c < 32; ++c) {
+    for (int c = 0; c < BN; ++c) {
       if (col0 + c < Tk) {
         const int set = p[col0 + c] != 0;
         any |= set;
@@ -486,7 +608,7 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   (void)R; (void)Hl; (void)D; (void)dtype;
   if (!has_mask || B <= 0 || Tq <= 0 || Tk <= 0) return 0;
   const int64_t bm = mask_batch_stride ? B : 1;
-  return size_t(bm * div_up(Tq, BM) * div_up(Tk, BN));
+  return size_t(bm * div_up(Tq, BM) * div_up(Tk, BN));   // one class byte per BM x BN tile
 }
 
 extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
@@ -513,13 +635,14 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (overlap(o, on, q, span_bytes(qs, R, B, Tq, Hl, D, eb)) || overlap(o, on, k, span_bytes(ks, R, B, tk1, Hl, D, eb)) ||
       overlap(o, on, v, span_bytes(vs, R, B, tk1, Hl, D, eb)))
     return SP_ERR_INVALID_ARG;
-  const int64_t nqt = div_up(Tq, BM), nkt = div_up(Tk, BN);
+  const int64_t nqt = div_up(Tq, dtype == SP_BF16 ? BM : BM32), nkt = div_up(Tk, BN);
+  const int64_t nqt_cls = div_up(Tq, BM);
   const int64_t nwg = nqt * Hl * B * R;
   if (nwg >= (int64_t(1) << 31) || nkt >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
   const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, has_mask, mask_batch_stride);
   if (has_mask && (workspace == nullptr || workspace_bytes < need)) return SP_ERR_INVALID_ARG;
-  if (has_mask && B > 65535) return SP_ERR_UNSUPPORTED;
+  if (has_mask && (B > 65535 || nqt_cls > 65535)) return SP_ERR_UNSUPPORTED;
 
   AttnArgs a;
   a.q = q; a.k = k; a.v = v; a.o = o;
@@ -532,14 +655,15 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   a.kv_end = kv_valid_len < Tk ? kv_valid_len : Tk;
   a.mask = mask; a.mask_bs = mask_batch_stride;
   a.cls = static_cast<const uint8_t*>(workspace);
-  a.nqt = int32_t(nqt); a.nkt = int32_t(nkt);
+  a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
   a.c = scale * 1.4426950408889634f;
   a.nwg = uint32_t(nwg);
   hipStream_t s = as_stream(stream);
   if (has_mask) {
     const int64_t bm = mask_batch_stride ? B : 1;
-    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt), unsigned(bm)), dim3(kThreads), 0, s,
-                       mask, mask_batch_stride, Tq, Tk, int32_t(nqt), int32_t(nkt), static_cast<uint8_t*>(workspace));
+    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt_cls), unsigned(bm)), dim3(kThreads), 0,
+                       s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
+                       static_cast<uint8_t*>(workspace));
     if (launch_status() != SP_OK) return SP_ERR_HIP;
     return dispatch_d<true>(D, a, dtype, s);
   }

@@ -112,9 +112,9 @@ def test_validation_returns_before_launch(lib):
 def test_workspace_size(lib):
     from sequence_attention_video_amd import binding as b
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == 0
-    # one byte per (128-row, 64-key) tile of the mask
-    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == 49 * 97
-    assert b.sp_masked_attention_workspace_size(1, 2, 256, 128, 4, 64, b.SP_BF16, True, 256 * 128) == 2 * 2 * 2
+    # one byte per (256-row, 64-key) tile of the mask
+    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == 25 * 97
+    assert b.sp_masked_attention_workspace_size(1, 2, 300, 128, 4, 64, b.SP_BF16, True, 300 * 128) == 2 * 2 * 2
 
 
 def test_fast_division_host_twin(tmp_path):
