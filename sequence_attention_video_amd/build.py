@@ -23,6 +23,10 @@ OBJ_DIR = os.path.join(PKG, "_build")
 
 SOURCES = ["sp_host.cpp", "sp_copy.hip", "sp_attention.hip"]
 ARCH = "gfx950"
+# Per-source compiler options.  The attention kernel keeps its MFMA results in
+# architectural VGPRs: the softmax reads them with VALU instructions, and the
+# default heuristic (AGPR results) costs a copy per element per tile.
+EXTRA_FLAGS = {"sp_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def hipcc() -> str:
@@ -43,7 +47,7 @@ def compile_flags() -> list[str]:
 def _compile(src: str) -> str:
     obj = os.path.join(OBJ_DIR, os.path.splitext(src)[0] + ".o")
     lang = ["-x", "hip"] if src.endswith(".hip") else []
-    cmd = [hipcc()] + compile_flags() + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [hipcc()] + compile_flags() + EXTRA_FLAGS.get(src, []) + lang + ["-c", os.path.join(CSRC, src), "-o", obj]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "'-packed-fp32-ops' is not a recognized feature"
     msgs = "\n".join(l for l in (res.stdout + res.stderr).splitlines() if noise not in l)

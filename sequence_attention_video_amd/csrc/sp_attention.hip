@@ -8,13 +8,16 @@
 // keys visible).
 //
 // Design (bf16):
-//   * one workgroup = 4 waves = 256 query rows of one (rank, batch, head), one
-//     wave per SIMD; each wave owns 64 query rows (two 32-row blocks) for the
-//     whole key loop, so every K or V operand read from LDS feeds two MFMAs
-//     (LDS reads run at about half of the LDS bandwidth at MFMA peak);
+//   * one workgroup = 8 waves = 256 query rows of one (rank, batch, head); each
+//     wave owns 32 query rows for the whole key loop, and two waves share each
+//     SIMD, so one wave's softmax (VALU) runs while the other's MFMAs do.  The
+//     kernel is templated on query blocks per wave (QB); two blocks per wave
+//     would let every LDS operand feed two MFMAs, but at D = 128 the registers
+//     then only allow one wave per SIMD, which measured slower;
 //   * key tiles of 64 are fetched with 16-byte direct global->LDS loads into a
-//     double buffer, one barrier per tile; the chunk order inside each row is
-//     XOR-swizzled so that the MFMA operand reads are bank-conflict free;
+//     double buffer, one barrier per tile; the tile is stored as padded 1 KiB
+//     key groups (see Bf16Tile) so that the MFMA operand reads are
+//     bank-conflict free and their addresses are a lane base plus immediates;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
 //     operand).  In the 32x32 accumulator layout a lane holds 16 keys of ONE
 //     query, so the row max/sum are in-lane plus one swap with lane^32, and the
@@ -22,13 +25,12 @@
 //     O^T += V^T P^T, whose accumulator again gives each lane one query: the
 //     softmax rescale is a per-lane scalar.  The V^T operand is read from the
 //     row-major V tile with the LDS transpose read ds_read_b64_tr_b16;
+//   * each tile is processed as two halves of 32 keys, which keeps the scores
+//     and probabilities of only 32 keys in registers;
 //   * softmax in float32 with exp2 (scale*log2 e folded into one FMA); the
-//     running max is only raised when a tile's max exceeds it by more than 2^8,
-//     so the O rescale runs rarely while p stays <= 256 (exact in float32,
+//     running max is only raised when a half's max exceeds it by more than
+//     2^8, so the O rescale runs rarely while p stays <= 256 (exact in float32,
 //     representable in bf16); row sums add the bf16-rounded p with v_dot2;
-//   * the two query blocks are software-pipelined inside the wave: the QK^T
-//     MFMAs of block 1 run under the exponentials of block 0, and the PV MFMAs
-//     of block 0 under the exponentials of block 1;
 //   * user masks are classified once per call into empty/full/partial tiles:
 //     empty tiles are skipped, full tiles read no mask bytes;
 //   * workgroup ids are remapped so that the 8 XCDs each take a contiguous run
@@ -45,6 +47,9 @@ namespace {
 constexpr int BM = 256;              // query rows per bf16 workgroup, and the mask-class tile height
 constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
+constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
+constexpr int BF16_WAVES = BM / (32 * QB);
+constexpr int BF16_THREADS = 64 * BF16_WAVES;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
@@ -132,12 +137,13 @@ struct Bf16Tile {
   static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int KPG = 512 / D;               // keys per 1 KiB group
   static constexpr int NG = BN / KPG;               // groups per tile = direct loads per tile
-  static constexpr int NLD = NG / 4;                // direct loads per wave per tile and tensor
+  static constexpr int NLD = NG / BF16_WAVES;       // direct loads per wave per tile and tensor
   static constexpr int GROUP_BYTES = 1024 + 64;
   static constexpr int TILE_BYTES = NG * GROUP_BYTES;
   static constexpr int NKS = D / 16;                // k-steps of QK^T
   static constexpr int NDB = D / 32;                // 32-row blocks of O^T
   static_assert(D == 64 || D == 128, "bf16 tiles are built for D = 64 and 128");
+  static_assert(NG % BF16_WAVES == 0, "every wave issues the same number of direct loads");
 
   static __host__ __device__ constexpr int pos(int n, int c) {
     return KPG == 8 ? ((n % KPG) ^ (4 * (c & 1))) : (n % KPG);
@@ -149,7 +155,7 @@ struct Bf16Tile {
 };
 
 template <int D, bool MASK>
-__global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   using T = Bf16Tile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD;
   __shared__ __attribute__((aligned(1024))) char k_lds0[T::TILE_BYTES];
@@ -167,12 +173,12 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   uint16_t* op = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
 
   // query rows of this lane: block qb covers rows 64*w + 32*qb .. +31 of the tile
-  int64_t qrow[2];
-  bool qvalid[2];
-  bf16x8 qf[2][NKS];
+  int64_t qrow[QB];
+  bool qvalid[QB];
+  bf16x8 qf[QB][NKS];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    qrow[qb] = int64_t(tc.qt) * BM + 64 * w + 32 * qb + l32;
+  for (int qb = 0; qb < QB; ++qb) {
+    qrow[qb] = int64_t(tc.qt) * BM + 32 * QB * w + 32 * qb + l32;
     qvalid[qb] = qrow[qb] < a.Tq;
 #pragma unroll
     for (int s = 0; s < NKS; ++s) {
@@ -181,21 +187,25 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  f32x16 oacc[2][NDB];
+  f32x16 oacc[QB][NDB];
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int d = 0; d < NDB; ++d) oacc[qb][d] = f32x16{};
-  float m_run[2] = {-1e30f, -1e30f};   // running max per query, log2 units
-  float l_run[2] = {0.f, 0.f};         // this lane's share of each denominator
+  float m_run[QB], l_run[QB];   // running max per query (log2 units); this lane's share of the sum
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    m_run[qb] = -1e30f;
+    l_run[qb] = 0.f;
+  }
 
   const uint8_t* cls_row = nullptr;
-  const uint8_t* mrow[2] = {nullptr, nullptr};
+  const uint8_t* mrow[QB] = {};
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) mrow[qb] = a.mask + tc.b * a.mask_bs + qrow[qb] * a.Tk;
+    for (int qb = 0; qb < QB; ++qb) mrow[qb] = a.mask + tc.b * a.mask_bs + qrow[qb] * a.Tk;
   }
   const int nkt_eff = int((a.kv_end + BN - 1) / BN);
   auto next_tile = [&](int kt) {
@@ -243,88 +253,82 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
   const int k_base = T::offset(l32, h);
   const int v_base = T::offset(4 * h + (s16 >> 2), 2 * dh + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
 
-  // One key tile on LDS buffers (kb_, vb_).
+  // One key tile on LDS buffers (kb_, vb_), as two halves of 32 keys: QK^T
+  // of the half for both query blocks, the online-softmax update, then PV.
   auto compute = [&](int kt, const char* kb_, const char* vb_) {
     const int64_t key0 = int64_t(kt) * BN;
     const uint8_t cls = MASK ? cls_row[kt] : uint8_t(kTileFull);
-    // S^T for both query blocks (keys x queries).  The K fragment (rows
-    // 32*kb + l32, chunk 2*ks + h) feeds both blocks.  Lane (l32, h), register v
-    // of half kb then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
-    f32x16 s[2][2];
+    const bool edge = (MASK && cls == kTilePartial) || key0 + BN > a.kv_end;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      s[0][kb] = f32x16{};
-      s[1][kb] = f32x16{};
+      // S^T of the half for both query blocks (keys x queries).  The K fragment
+      // (key 32*kb + l32, chunk 2*ks + h) feeds both blocks.  Lane (l32, h),
+      // register v then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
+      f32x16 s[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         // offset(32*kb + l32, 2*ks + h) - offset(l32, h) is lane-independent
         const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
             kb_ + k_base + (T::offset(32 * kb, 2 * ks) - T::offset(0, 0)));
-        s[0][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[0][ks], s[0][kb], 0, 0, 0);
-        s[1][kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[1][ks], s[1][kb], 0, 0, 0);
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb)
+          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
       }
-    }
-    if ((MASK && cls == kTilePartial) || key0 + BN > a.kv_end) {
-      // register v of half kb is key key0 + 4*h + kofs(kb, v)
-      const int room = int(a.kv_end - key0) - 4 * h;   // visible iff kofs < room
+      if (edge) {
+        // visible iff key < kv_end (and the mask byte is set on partial tiles)
+        const int room = int(a.kv_end - key0) - 4 * h - 32 * kb;
 #pragma unroll
-      for (int qb = 0; qb < 2; ++qb) {
-        const uint8_t* mk = MASK ? mrow[qb] + key0 + 4 * h : nullptr;
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
+        for (int qb = 0; qb < QB; ++qb) {
+          const uint8_t* mk = MASK ? mrow[qb] + key0 + 32 * kb + 4 * h : nullptr;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int kofs = 32 * kb + 8 * (v >> 2) + (v & 3);
+            const int kofs = 8 * (v >> 2) + (v & 3);
             bool vis = kofs < room;
             if (MASK && cls == kTilePartial && vis) vis = qvalid[qb] && mk[kofs] != 0;
-            if (!vis) s[qb][kb][v] = -INFINITY;
+            if (!vis) s[qb][v] = -INFINITY;
           }
+        }
       }
-    }
-    // softmax numerators, rounded to bf16: the B operands of the PV MFMA
-    bf16x8 pf[2][2][2];
+      // softmax numerators, rounded to bf16: the B operands of the PV MFMA
+      bf16x8 pf[QB][2];
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      float mx = -INFINITY;
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][v]);
+        const float mxc = wave_max_pair(mx) * a.c;
+        if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_run[qb], mxc);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          l_run[qb] *= alpha;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][kb][v]);
-      const float mxc = wave_max_pair(mx) * a.c;
-      if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
-        const float m_new = fmaxf(m_run[qb], mxc);
-        const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-        l_run[qb] *= alpha;
-#pragma unroll
-        for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
-        m_run[qb] = m_new;
-      }
-      const float nm = -m_run[qb];
-      float part[2] = {0.f, 0.f};
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+          for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
+          m_run[qb] = m_new;
+        }
+        const float nm = -m_run[qb];
+        float part = 0.f;
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
           for (int e = 0; e < 8; ++e)
-            pf[qb][kb][j2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][kb][8 * j2 + e], a.c, nm)));
+            pf[qb][j2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * j2 + e], a.c, nm)));
 #pragma unroll
           for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pair = {pf[qb][kb][j2][e], pf[qb][kb][j2][e + 1]};
-            part[j2] = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part[j2], false);
+            const bf16x2 pair = {pf[qb][j2][e], pf[qb][j2][e + 1]};
+            part = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part, false);
           }
         }
-      l_run[qb] += part[0] + part[1];
-    }
-    // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
-    // of half-tile kb.  The V^T operand takes the same keys through two transpose
-    // reads: in each 16-lane group, source lane s addresses key k0 + s/4 at dims
-    // n0 + 4*(s%4) .. +3, and lane j receives dim n0 + j of keys k0 .. k0+3
-    // (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
+        l_run[qb] += part;
+      }
+      // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
+      // of the half.  The V^T operand takes the same keys through two transpose
+      // reads: in each 16-lane group, source lane s addresses key k0 + s/4 at dims
+      // n0 + 4*(s%4) .. +3, and lane j receives dim n0 + j of keys k0 .. k0+3
+      // (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
 #pragma unroll
-    for (int d = 0; d < NDB; ++d) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+      for (int d = 0; d < NDB; ++d) {
 #pragma unroll
         for (int j2 = 0; j2 < 2; ++j2) {
           constexpr int z = T::offset(0, 0);
@@ -334,9 +338,10 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + v_base + o1));
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
-          for (int qb = 0; qb < 2; ++qb)
-            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][kb][j2], oacc[qb][d], 0, 0, 0);
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][j2], oacc[qb][d], 0, 0, 0);
         }
+      }
     }
   };
 
@@ -365,7 +370,7 @@ __global__ __launch_bounds__(kThreads) void attn_bf16_kernel(AttnArgs a) {
 
   // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4
 #pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
+  for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     const float inv = lt > 0.f ? 1.0f / lt : 0.f;
     if (qvalid[qb]) {
@@ -577,7 +582,7 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 template <int D, bool MASK>
 void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
   if (dt == SP_BF16) {
-    if constexpr (D % 32 == 0) hipLaunchKernelGGL((attn_bf16_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
+    if constexpr (D % 32 == 0) hipLaunchKernelGGL((attn_bf16_kernel<D, MASK>), dim3(a.nwg), dim3(BF16_THREADS), 0, s, a);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
   }
