@@ -141,8 +141,9 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * mask: device (B, Tq, Tk) uint8, rows packed (row stride Tk), batch stride
  * mask_batch_stride (0 = one mask for every batch), or NULL for the key-only
  * padding mask.  The mask is shared by every rank and head.
- * workspace: device scratch of sp_masked_attention_workspace_size() bytes (the
- * per-tile mask classes); may be NULL when that size is 0.
+ * workspace: device scratch of sp_masked_attention_workspace_size() bytes,
+ * 256-byte aligned (per-tile mask classes and bit-packed mask rows, rewritten
+ * by every call); may be NULL when that size is 0.
  * Supported: SP_BF16 with D in {64, 128} (bf16 MFMA, float32 softmax and
  * accumulation, output rounded to nearest even) and SP_F32 with D in
  * {16, 64, 128} (float32 MFMA throughout).

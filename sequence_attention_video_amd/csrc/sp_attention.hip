@@ -14,8 +14,9 @@
 //     kernel is templated on query blocks per wave (QB); two blocks per wave
 //     would let every LDS operand feed two MFMAs, but at D = 128 the registers
 //     then only allow one wave per SIMD, which measured slower;
-//   * key tiles of 64 are fetched with 16-byte direct global->LDS loads into a
-//     double buffer, one barrier per tile; the tile is stored as padded 1 KiB
+//   * key tiles of KT = 128 are fetched with 16-byte direct global->LDS loads
+//     into a double buffer (NBUF stages in general), one barrier per tile, and
+//     the next tile's loads overlap this tile's compute; the tile is stored as padded 1 KiB
 //     key groups (see Bf16Tile) so that the MFMA operand reads are
 //     bank-conflict free and their addresses are a lane base plus immediates;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
@@ -25,8 +26,8 @@
 //     O^T += V^T P^T, whose accumulator again gives each lane one query: the
 //     softmax rescale is a per-lane scalar.  The V^T operand is read from the
 //     row-major V tile with the LDS transpose read ds_read_b64_tr_b16;
-//   * each tile is processed as two halves of 32 keys, which keeps the scores
-//     and probabilities of only 32 keys in registers;
+//   * each tile is processed in parts of 32 keys, which keeps the scores and
+//     probabilities of only 32 keys in registers;
 //   * softmax in float32 with exp2 (scale*log2 e folded into one FMA); the
 //     running max is only raised when a half's max exceeds it by more than
 //     2^8, so the O rescale runs rarely while p stays <= 256 (exact in float32,
@@ -40,6 +41,7 @@
 #include "sp_internal.h"
 
 #include <cmath>
+#include <type_traits>
 
 namespace sp {
 namespace {
@@ -48,6 +50,8 @@ constexpr int BM = 256;              // query rows per bf16 workgroup, and the m
 constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
+constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
+constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
 constexpr int BF16_WAVES = BM / (32 * QB);
 constexpr int BF16_THREADS = 64 * BF16_WAVES;
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
@@ -76,6 +80,7 @@ struct AttnArgs {
   const uint8_t* mask;                   // (B, Tq, Tk) or null
   int64_t mask_bs;                       // batch stride of mask (0 = shared)
   const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt), BM x BN tiles
+  const uint64_t* bits;                  // visibility words (Bm, Tq, nkt): bit j = key BN*kt + j
   int32_t nqt, nkt;                      // query tiles of this kernel, key tiles of BN
   int32_t nqt_cls;                       // query tiles of the class map (height BM)
   float c;                               // scale * log2(e)
@@ -121,7 +126,7 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 // expcnt and lgkmcnt fields are left at their maximum, i.e. not waited on).
 __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
-// LDS layout of one K or V tile (BN keys x D dims, bf16).  The tile is cut
+// LDS layout of one K or V tile (KT keys x D dims, bf16).  The tile is cut
 // into groups of KPG keys whose rows make exactly 1 KiB (KPG = 4 at D = 128,
 // 8 at D = 64); one 16-byte direct load of a wave (64 lanes) fills one group,
 // reading KPG whole rows.  Groups sit GROUP_BYTES apart (1 KiB + 64 B of
@@ -134,9 +139,8 @@ __device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70)
 // compile-time offset.
 template <int D>
 struct Bf16Tile {
-  static constexpr int CPR = D / 8;                 // 16-byte chunks per row
   static constexpr int KPG = 512 / D;               // keys per 1 KiB group
-  static constexpr int NG = BN / KPG;               // groups per tile = direct loads per tile
+  static constexpr int NG = KT / KPG;               // groups per tile = direct loads per tile
   static constexpr int NLD = NG / BF16_WAVES;       // direct loads per wave per tile and tensor
   static constexpr int GROUP_BYTES = 1024 + 64;
   static constexpr int TILE_BYTES = NG * GROUP_BYTES;
@@ -144,6 +148,7 @@ struct Bf16Tile {
   static constexpr int NDB = D / 32;                // 32-row blocks of O^T
   static_assert(D == 64 || D == 128, "bf16 tiles are built for D = 64 and 128");
   static_assert(NG % BF16_WAVES == 0, "every wave issues the same number of direct loads");
+  static_assert(2 * NBUF * TILE_BYTES <= 160 * 1024, "K and V buffers must fit the 160 KiB LDS");
 
   static __host__ __device__ constexpr int pos(int n, int c) {
     return KPG == 8 ? ((n % KPG) ^ (4 * (c & 1))) : (n % KPG);
@@ -154,14 +159,35 @@ struct Bf16Tile {
   }
 };
 
+// s_waitcnt with vmcnt = n and expcnt / lgkmcnt left at their maximum.
+template <int N>
+__device__ __forceinline__ void wait_vmem() {
+  static_assert(N >= 0 && N < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
+}
+
 template <int D, bool MASK>
 __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   using T = Bf16Tile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD;
+  constexpr int LOADS = 2 * NLD;   // direct loads per wave per tile (K and V)
+  // Each buffer is its own LDS object, so that the compiler can tell which
+  // buffer a direct load writes and never waits on it before reading another.
   __shared__ __attribute__((aligned(1024))) char k_lds0[T::TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) char k_lds1[T::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds0[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds1[T::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char v_lds1[T::TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) char k_lds2[NBUF > 2 ? T::TILE_BYTES : 16];
+  __shared__ __attribute__((aligned(1024))) char v_lds2[NBUF > 2 ? T::TILE_BYTES : 16];
+  auto kbuf = [&](auto i) __attribute__((always_inline)) -> char* {
+    constexpr int I = decltype(i)::value;
+    return I == 0 ? k_lds0 : (I == 1 ? k_lds1 : k_lds2);
+  };
+  auto vbuf = [&](auto i) __attribute__((always_inline)) -> char* {
+    constexpr int I = decltype(i)::value;
+    return I == 0 ? v_lds0 : (I == 1 ? v_lds1 : v_lds2);
+  };
+  using I0 = std::integral_constant<int, 0>;
 
   const TileCoord tc = decode_tile<MASK>(a);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -172,7 +198,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   const uint16_t* vp = static_cast<const uint16_t*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
   uint16_t* op = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
 
-  // query rows of this lane: block qb covers rows 64*w + 32*qb .. +31 of the tile
+  // query rows of this lane: block qb covers rows 32*QB*w + 32*qb .. +31 of the tile
   int64_t qrow[QB];
   bool qvalid[QB];
   bf16x8 qf[QB][NKS];
@@ -200,18 +226,32 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   }
 
   const uint8_t* cls_row = nullptr;
-  const uint8_t* mrow[QB] = {};
+  const uint64_t* brow[QB] = {};
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mrow[qb] = a.mask + tc.b * a.mask_bs + qrow[qb] * a.Tk;
+    for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + (bm * a.Tq + (qvalid[qb] ? qrow[qb] : 0)) * int64_t(a.nkt);
   }
-  const int nkt_eff = int((a.kv_end + BN - 1) / BN);
-  auto next_tile = [&](int kt) {
+  // Key tiles of KT keys; with a user mask a tile's class combines the classes
+  // of its BN-key class tiles, and empty tiles are skipped.
+  const int nkt_eff = int((a.kv_end + KT - 1) / KT);
+  auto tile_class = [&](int kt) __attribute__((always_inline)) -> uint8_t {
+    if (!MASK) return kTileFull;
+    bool any = false, all = true;
+#pragma unroll
+    for (int i = 0; i < KT / BN; ++i) {
+      const int c = kt * (KT / BN) + i;
+      const uint8_t v = c < a.nkt ? cls_row[c] : uint8_t(kTileEmpty);
+      any |= v != kTileEmpty;
+      all &= v == kTileFull;
+    }
+    return !any ? kTileEmpty : (all ? kTileFull : kTilePartial);
+  };
+  auto next_tile = [&](int kt) __attribute__((always_inline)) {
     ++kt;
     if (MASK)
-      while (kt < nkt_eff && cls_row[kt] == kTileEmpty) ++kt;
+      while (kt < nkt_eff && tile_class(kt) == kTileEmpty) ++kt;
     return kt;
   };
 
@@ -225,9 +265,9 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   const int wu = __builtin_amdgcn_readfirstlane(w);          // wave index, as a scalar
   const int64_t k_lane = int64_t(ld_n) * a.ks[2] + 8 * ld_c;
   const int64_t v_lane = int64_t(ld_n) * a.vs[2] + 8 * ld_c;
-  auto issue = [&](int kt, char* kdst, char* vdst) {
-    const int64_t key0 = int64_t(kt) * BN;
-    if (key0 + BN <= a.kv_end) {
+  auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
+    const int64_t key0 = int64_t(kt) * KT;
+    if (key0 + KT <= a.kv_end) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int grp = wu * NLD + j;
@@ -253,17 +293,28 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   const int k_base = T::offset(l32, h);
   const int v_base = T::offset(4 * h + (s16 >> 2), 2 * dh + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
 
-  // One key tile on LDS buffers (kb_, vb_), as two halves of 32 keys: QK^T
-  // of the half for both query blocks, the online-softmax update, then PV.
-  auto compute = [&](int kt, const char* kb_, const char* vb_) {
-    const int64_t key0 = int64_t(kt) * BN;
-    const uint8_t cls = MASK ? cls_row[kt] : uint8_t(kTileFull);
-    const bool edge = (MASK && cls == kTilePartial) || key0 + BN > a.kv_end;
+  // One key tile on LDS buffers (kb_, vb_), in parts of 32 keys: QK^T of the
+  // part, the online-softmax update, then PV.
+  auto compute = [&](int kt, const char* kb_, const char* vb_) __attribute__((always_inline)) {
+    const int64_t key0 = int64_t(kt) * KT;
+    const uint8_t cls = tile_class(kt);
+    const bool edge = (MASK && cls == kTilePartial) || key0 + KT > a.kv_end;
+    // visibility words of this lane's rows for the BN-key class tiles of this tile
+    uint64_t mw[QB][KT / BN];
+    if (MASK && cls == kTilePartial) {
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      // S^T of the half for both query blocks (keys x queries).  The K fragment
-      // (key 32*kb + l32, chunk 2*ks + h) feeds both blocks.  Lane (l32, h),
-      // register v then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
+      for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+        for (int c = 0; c < KT / BN; ++c) {
+          const int ct = kt * (KT / BN) + c;
+          mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][ct] : 0ull;
+        }
+    }
+#pragma unroll
+    for (int kb = 0; kb < KT / 32; ++kb) {
+      // S^T of the part (keys x queries).  The K fragment (key 32*kb + l32,
+      // chunk 2*ks + h) feeds every query block.  Lane (l32, h), register v
+      // then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
       f32x16 s[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
@@ -277,16 +328,17 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
       }
       if (edge) {
-        // visible iff key < kv_end (and the mask byte is set on partial tiles)
+        // visible iff key < kv_end (and its mask bit is set on partial tiles)
         const int room = int(a.kv_end - key0) - 4 * h - 32 * kb;
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
-          const uint8_t* mk = MASK ? mrow[qb] + key0 + 32 * kb + 4 * h : nullptr;
+          // bit 8*(v/4) + v%4 of wsh is register v's key
+          const uint32_t wsh = MASK ? uint32_t(mw[qb][kb / 2] >> (32 * (kb & 1) + 4 * h)) : 0u;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kofs = 8 * (v >> 2) + (v & 3);
             bool vis = kofs < room;
-            if (MASK && cls == kTilePartial && vis) vis = qvalid[qb] && mk[kofs] != 0;
+            if (MASK && cls == kTilePartial) vis = vis && ((wsh >> kofs) & 1u);
             if (!vis) s[qb][v] = -INFINITY;
           }
         }
@@ -323,7 +375,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
         l_run[qb] += part;
       }
       // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
-      // of the half.  The V^T operand takes the same keys through two transpose
+      // of the part.  The V^T operand takes the same keys through two transpose
       // reads: in each 16-lane group, source lane s addresses key k0 + s/4 at dims
       // n0 + 4*(s%4) .. +3, and lane j receives dim n0 + j of keys k0 .. k0+3
       // (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
@@ -345,27 +397,45 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     }
   };
 
-  // Double-buffered tile loop, unrolled by two so that each LDS buffer is a
-  // distinct object: loads of the next tile overlap the compute of this one,
-  // and one barrier per tile separates the buffer reuse.
-  int kt = MASK ? next_tile(-1) : 0;
-  if (kt < nkt_eff) issue(kt, k_lds0, v_lds0);
-  wait_vmem();
-  __syncthreads();
-  while (kt < nkt_eff) {
-    int kn = next_tile(kt);
-    if (kn < nkt_eff) issue(kn, k_lds1, v_lds1);
-    compute(kt, k_lds0, v_lds0);
-    wait_vmem();
+  // NBUF-stage pipeline over the tiles, unrolled by NBUF so that every LDS
+  // buffer is a constant index (the compiler then knows which buffer each
+  // direct load writes and does not wait on them before unrelated LDS reads).
+  // Iteration i: wait for tile i's loads, barrier (tile i visible to all waves;
+  // every wave done with tile i-1), issue tile i+NBUF-1 into tile i-1's
+  // buffer, compute tile i.
+  int ahead[NBUF];   // tiles i .. i+NBUF-1
+  ahead[0] = MASK ? next_tile(-1) : 0;
+#pragma unroll
+  for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff);
+  if (ahead[0] < nkt_eff) issue(ahead[0], kbuf(I0{}), vbuf(I0{}));
+  if constexpr (NBUF > 2) {
+    if (ahead[1] < nkt_eff) issue(ahead[1], kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
+  }
+  auto stage = [&](auto sidx) __attribute__((always_inline)) -> bool {
+    constexpr int S = decltype(sidx)::value;
+    const int kt = ahead[0];
+    if (kt >= nkt_eff) return false;
+    // loads still allowed in flight: those of the tiles issued after tile i
+    int later = 0;
+#pragma unroll
+    for (int j = 1; j < NBUF - 1; ++j) later += ahead[j] < nkt_eff;
+    if (later == NBUF - 2) wait_vmem<LOADS * (NBUF - 2)>();
+    else wait_vmem<0>();
     __syncthreads();
-    kt = kn;
-    if (kt >= nkt_eff) break;
-    kn = next_tile(kt);
-    if (kn < nkt_eff) issue(kn, k_lds0, v_lds0);
-    compute(kt, k_lds1, v_lds1);
-    wait_vmem();
-    __syncthreads();
-    kt = kn;
+#pragma unroll
+    for (int j = 0; j < NBUF - 1; ++j) ahead[j] = ahead[j + 1];
+    ahead[NBUF - 1] = next_tile(ahead[NBUF - 2] < nkt_eff ? ahead[NBUF - 2] : nkt_eff);
+    using NX = std::integral_constant<int, (S + NBUF - 1) % NBUF>;
+    if (ahead[NBUF - 2] < nkt_eff) issue(ahead[NBUF - 2], kbuf(NX{}), vbuf(NX{}));
+    compute(kt, kbuf(sidx), vbuf(sidx));
+    return true;
+  };
+  for (;;) {
+    if (!stage(std::integral_constant<int, 0>{})) break;
+    if (!stage(std::integral_constant<int, 1>{})) break;
+    if constexpr (NBUF > 2) {
+      if (!stage(std::integral_constant<int, 2>{})) break;
+    }
   }
 
   // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4
@@ -535,25 +605,45 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- mask tiles
 
-// One workgroup per (batch, q-tile, k-tile): reads the tile's in-range mask
-// bytes once and records whether none, all, or some of them are set.
+// One workgroup per (batch, q-tile, k-tile), one mask row per thread: reads
+// the row's BN bytes of the tile (as wide as their alignment allows), writes
+// them as one 64-bit visibility word (bit j = key BN*kt + j), and records
+// whether none, all, or some of the tile's in-range bytes are set.
+__device__ __forceinline__ uint64_t nonzero_bytes_to_bits(uint64_t x) {
+  // bit j of the result = (byte j of x != 0)
+  uint64_t r = 0;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) r |= uint64_t(((x >> (8 * j)) & 0xffu) != 0) << j;
+  return r;
+}
+
 __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
-                                                               int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls) {
+                                                               int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
+                                                               uint64_t* bits) {
   static_assert(BM == kThreads, "one mask row per thread");
+  static_assert(BN == 64, "one 64-bit word per row and tile");
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int64_t row = int64_t(qt) * BM + threadIdx.x;
   const int64_t col0 = int64_t(kt) * BN;
+  const int n = int(Tk - col0 < BN ? Tk - col0 : BN);           // in-range keys of the tile
+  const uint64_t full = n == 64 ? ~0ull : ((1ull << n) - 1);
   int any = 0, all = 1;
   if (row < Tq) {
-    const uint8_t* p = mask + b * mask_bs + row * Tk;
-    for (int c = 0; c < BN; ++c) {
-      if (col0 + c < Tk) {
-        const int set = p[col0 + c] != 0;
-        any |= set;
-        all &= set;
-      }
+    const uint8_t* p = mask + b * mask_bs + row * Tk + col0;
+    uint64_t word = 0;
+    if (n == BN && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) word |= nonzero_bytes_to_bits(reinterpret_cast<const uint64_t*>(p)[i]) << (8 * i);
+    } else if (n == BN && (reinterpret_cast<uintptr_t>(p) & 3) == 0) {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) word |= nonzero_bytes_to_bits(reinterpret_cast<const uint32_t*>(p)[i]) << (4 * i);
+    } else {
+      for (int c = 0; c < n; ++c) word |= uint64_t(p[c] != 0) << c;
     }
+    bits[(b * Tq + row) * int64_t(nkt) + kt] = word;
+    any = word != 0;
+    all = word == full;
   }
   any = __syncthreads_or(any);
   all = __syncthreads_and(all);
@@ -613,7 +703,10 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   (void)R; (void)Hl; (void)D; (void)dtype;
   if (!has_mask || B <= 0 || Tq <= 0 || Tk <= 0) return 0;
   const int64_t bm = mask_batch_stride ? B : 1;
-  return size_t(bm * div_up(Tq, BM) * div_up(Tk, BN));   // one class byte per BM x BN tile
+  // one class byte per BM x BN tile, then (256-byte aligned) one 64-bit
+  // visibility word per mask row and BN-key tile
+  const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
+  return size_t(cls_bytes + bm * Tq * div_up(Tk, BN) * 8);
 }
 
 extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
@@ -647,6 +740,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   const bool has_mask = mask != nullptr && Tk > 0;
   const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, has_mask, mask_batch_stride);
   if (has_mask && (workspace == nullptr || workspace_bytes < need)) return SP_ERR_INVALID_ARG;
+  if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
   if (has_mask && (B > 65535 || nqt_cls > 65535)) return SP_ERR_UNSUPPORTED;
 
   AttnArgs a;
@@ -660,6 +754,11 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   a.kv_end = kv_valid_len < Tk ? kv_valid_len : Tk;
   a.mask = mask; a.mask_bs = mask_batch_stride;
   a.cls = static_cast<const uint8_t*>(workspace);
+  {
+    const int64_t bm = mask_batch_stride ? B : 1;
+    const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
+    a.bits = reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + cls_bytes);
+  }
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
   a.c = scale * 1.4426950408889634f;
   a.nwg = uint32_t(nwg);
@@ -668,7 +767,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
     const int64_t bm = mask_batch_stride ? B : 1;
     hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt_cls), unsigned(bm)), dim3(kThreads), 0,
                        s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
-                       static_cast<uint8_t*>(workspace));
+                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits));
     if (launch_status() != SP_OK) return SP_ERR_HIP;
     return dispatch_d<true>(D, a, dtype, s);
   }

@@ -112,9 +112,12 @@ def test_validation_returns_before_launch(lib):
 def test_workspace_size(lib):
     from sequence_attention_video_amd import binding as b
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == 0
-    # one byte per (256-row, 64-key) tile of the mask
-    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == 25 * 97
-    assert b.sp_masked_attention_workspace_size(1, 2, 300, 128, 4, 64, b.SP_BF16, True, 300 * 128) == 2 * 2 * 2
+    # one class byte per (256-row, 64-key) tile of the mask, padded to 256 bytes,
+    # then one 64-bit word per mask row and 64-key tile
+    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == \
+        2560 + 6152 * 97 * 8
+    assert b.sp_masked_attention_workspace_size(1, 2, 300, 128, 4, 64, b.SP_BF16, True, 300 * 128) == \
+        256 + 2 * 300 * 2 * 8
 
 
 def test_fast_division_host_twin(tmp_path):
