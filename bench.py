@@ -60,6 +60,111 @@ def read_traffic(workload: str, src_hash: str):
     return rec.get("bytes_per_launch")
 
 
+COPY_PROBE_BYTES = 1 << 29   # plain device copy of known size for counter calibration
+
+
+def traffic_probe(workload: str, launches: int = 3):
+    """Run only what the HBM counter passes measure: one plain copy of
+    COPY_PROBE_BYTES (calibration), then the step once and the attention
+    kernel `launches` more times."""
+    import numpy as np
+    import torch
+
+    from sequence_attention_video_amd.pipeline import UlyssesStep
+    from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS[workload]
+    x = make_inputs(wl)
+    td = lambda a: (torch.from_numpy(a).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)).cuda()
+    src = torch.empty(COPY_PROBE_BYTES, dtype=torch.uint8, device="cuda").random_()
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    step = UlyssesStep(wl, td(x["q"]), td(x["k"]), td(x["v"]), td(x["mask"]) if x["mask"] is not None else None)
+    step.run()
+    for _ in range(launches):
+        step.attention()
+    torch.cuda.synchronize()
+    print("traffic probe done", workload, flush=True)
+
+
+def _counter_rows(path):
+    import csv
+    import glob
+    files = glob.glob(os.path.join(path, "**", "*counter_collection.csv"), recursive=True)
+    rows = []
+    for f in files:
+        rows += list(csv.DictReader(open(f)))
+    return rows
+
+
+def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: list):
+    """Turn the two counter passes into profiles/attention_traffic_<workload>.md."""
+    import collections
+    out = {}
+    for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
+        per = collections.defaultdict(float)
+        kname = {}
+        for r in _counter_rows(d):
+            if r["Counter_Name"] != name:
+                continue
+            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
+            kname[r["Dispatch_Id"]] = r["Kernel_Name"]
+        copy = [per[i] for i in per if "copy" in kname[i].lower() and "attn" not in kname[i]]
+        attn = [per[i] for i in per if "attn_bf16_kernel" in kname[i] or "attn_f32_kernel" in kname[i]]
+        relay = [per[i] for i in per if "relayout_kernel" in kname[i]]
+        copy_kib = max(copy) if copy else float("nan")
+        scale = (COPY_PROBE_BYTES / 1024.0) / copy_kib        # true KiB per counted KiB
+        out[name] = {"copy_kib": copy_kib, "scale": scale,
+                     "attention_kib": sum(attn[1:]) / max(1, len(attn[1:])) if len(attn) > 1 else (attn[0] if attn else float("nan")),
+                     "relayout_kib": relay[0] if relay else float("nan")}
+    fetch_b = out["FETCH_SIZE"]["attention_kib"] * out["FETCH_SIZE"]["scale"] * 1024
+    write_b = out["WRITE_SIZE"]["attention_kib"] * out["WRITE_SIZE"]["scale"] * 1024
+    rec = {"workload": workload, "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
+           "bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "fetch_scale": out["FETCH_SIZE"]["scale"], "write_scale": out["WRITE_SIZE"]["scale"]}
+    lines = [f"# HBM traffic of the attention kernel on {workload}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```"] + cmds + ["```", "",
+             f"Calibration: a plain {COPY_PROBE_BYTES >> 20} MiB device copy read "
+             f"{out['FETCH_SIZE']['copy_kib']:.0f} KiB (FETCH_SIZE) and wrote {out['WRITE_SIZE']['copy_kib']:.0f} KiB "
+             f"(WRITE_SIZE) against {COPY_PROBE_BYTES >> 10} KiB moved, so the counters are scaled by "
+             f"{out['FETCH_SIZE']['scale']:.3f} and {out['WRITE_SIZE']['scale']:.3f}.", "",
+             "| counter | attention, KiB per launch (raw) | scaled bytes per launch |", "|---|---|---|",
+             f"| FETCH_SIZE | {out['FETCH_SIZE']['attention_kib']:.0f} | {fetch_b:.4g} |",
+             f"| WRITE_SIZE | {out['WRITE_SIZE']['attention_kib']:.0f} | {write_b:.4g} |", "",
+             "traffic_json: " + json.dumps(rec)]
+    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
+def write_kernel_trace_summary(stats_csv: str, bench_json: str, title: str, cmd: str, out_name: str):
+    """Turn a rocprofv3 --stats kernel_stats.csv (and the bench line of the same
+    run) into a short markdown summary under profiles/."""
+    import csv
+    rows = list(csv.DictReader(open(stats_csv)))
+    bench = json.loads(open(bench_json).read())
+    lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
+             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        name = r["Name"].replace("sp::(anonymous namespace)::", "")
+        name = name if len(name) <= 90 else name[:87] + "..."
+        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | {float(r['MinNs'])/1e3:.1f} | "
+                     f"{float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f}% |")
+    k = bench["kernels"]
+    lines += ["", "The same run's bench line (HIP events on the launch stream):", "",
+              f"* masked attention: {k['masked_attention']['ms']*1e3:.1f} us per launch, "
+              f"{k['masked_attention']['TFLOP/s']} TFLOP/s ({100*k['masked_attention']['mfma_frac']:.1f}% of the MFMA peak)",
+              f"* send_recv_heads (Q, K, V, rotating buffers): {k['send_recv_heads_rotating']['ms']*1e3:.1f} us, "
+              f"{k['send_recv_heads_rotating']['GB/s']} GB/s ({100*k['send_recv_heads_rotating']['hbm_frac']:.1f}% of 8000 GB/s)",
+              f"* kernel source hash: `{bench['kernel_source_hash']}`"]
+    path = os.path.join(ROOT, "profiles", out_name)
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -68,7 +173,26 @@ def main():
     ap.add_argument("--config", default="video_self")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--traffic-probe", action="store_true",
+                    help="run only a calibration copy and attention launches (for rocprofv3 --pmc passes)")
+    ap.add_argument("--write-traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/attention_traffic_<config>.md from two counter passes")
+    ap.add_argument("--write-kernel-trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
+                    help="write profiles/kernel_trace_<config>.md from a rocprofv3 --stats run of bench.py")
+    ap.add_argument("--profile-command", action="append", default=[],
+                    help="the command line(s) that produced the profile, recorded in the summary")
     args = ap.parse_args()
+    if args.write_traffic_summary:
+        write_traffic_summary(args.config, *args.write_traffic_summary, args.profile_command)
+        return
+    if args.write_kernel_trace_summary:
+        write_kernel_trace_summary(*args.write_kernel_trace_summary,
+                                   f"rocprofv3 kernel trace: bench step on {args.config}",
+                                   "\n".join(args.profile_command), f"kernel_trace_{args.config}.md")
+        return
+    if args.traffic_probe:
+        traffic_probe(args.config)
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -271,9 +395,8 @@ def cpu_baseline(wl, x, budget_s: float):
     rows_done = 0
     heads_done = []
     t0 = time.perf_counter()
-    for j in range(Hl):                          # rank 0 owns heads 0..Hl-1
-        kj = widen(O.pad_tokens(x["k"][:, :, j], Tp)[0]) if not wl.cross else widen(
-            O.pad_tokens(x["k"][:, :, j], Tp)[0])
+    for j in range(wl.H):                        # rank 0's heads first, then rank 1's, ...
+        kj = widen(O.pad_tokens(x["k"][:, :, j], Tp)[0])
         vj = widen(O.pad_tokens(x["v"][:, :, j], Tp)[0])
         qsrc = x["q"][0, :, j] if wl.cross else O.pad_tokens(x["q"][:, :, j], Tp)[0]
         nq = qsrc.shape[0]
@@ -292,8 +415,9 @@ def cpu_baseline(wl, x, budget_s: float):
             break
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows of rank 0's heads {heads_done} against all "
-                      f"{Tp} keys, float64 NumPy oracle, {dt:.1f} s",
+            "sample": f"{rows_done} query rows (batch 0; heads {heads_done[0]}..{heads_done[-1]}, rank-major) "
+                      f"against all {Tp} keys, float64 NumPy oracle, {dt:.1f} s; the full step is "
+                      f"{wl.H * wl.B} such heads",
             "seconds": round(dt, 2)}
 
 

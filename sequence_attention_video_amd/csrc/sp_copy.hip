@@ -2,7 +2,9 @@
 // extension), the token<->head relayout of the virtual ranks, and
 // gather/unpad.  All three are HBM-bound byte moves: every thread moves 16-byte
 // vectors, a wave covers 1 KiB of contiguous destination per instruction, and
-// no value is ever converted, so results are bit-exact by construction.
+// no value is ever converted, so results are bit-exact by construction.  Loads
+// and stores are non-temporal (each byte is touched once, so keeping it in the
+// caches only evicts useful lines): measured +15 % on the Q/K/V relayout.
 //
 // Sources: page "LTX-2 序列并行拆解：token 切分、all2all 换头与 runner 接入全链路",
 // section "token 切片、换头、gather 还原", steps 补齐 (pad), 换头 (head swap) and
@@ -18,7 +20,14 @@ constexpr int64_t kChunk = int64_t(kThreads) * kUnroll;
 constexpr int kMaxWorld = 128;                     // ranks per gather_unpad launch
 constexpr int kMaxGridY = 65535;
 
-using vec16 = uint4;
+typedef unsigned int vec16 __attribute__((ext_vector_type(4)));   // one 16-byte vector
+
+__device__ __forceinline__ vec16 load16(const char* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const vec16*>(p));
+}
+__device__ __forceinline__ void store16(char* p, vec16 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<vec16*>(p));
+}
 
 // ------------------------------------------------------------------ relayout
 
@@ -66,13 +75,13 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
       const int64_t head = head_off + int64_t(f) * 16;
       const int64_t raddr = a.to_heads ? tok : head;
       waddr[u] = a.to_heads ? head : tok;
-      buf[u] = *reinterpret_cast<const vec16*>(src + raddr);
+      buf[u] = load16(src + raddr);
     }
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_seg) *reinterpret_cast<vec16*>(dst + waddr[u]) = buf[u];
+    if (f < a.n_per_seg) store16(dst + waddr[u], buf[u]);
   }
 }
 
@@ -97,13 +106,13 @@ __global__ __launch_bounds__(kThreads) void pad_tokens_kernel(PadArgs a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t f = f0 + u * kThreads;
-    buf[u] = make_uint4(0, 0, 0, 0);
-    if (f < a.copy_vecs) buf[u] = *reinterpret_cast<const vec16*>(x + f * 16);
+    buf[u] = vec16{0, 0, 0, 0};
+    if (f < a.copy_vecs) buf[u] = load16(x + f * 16);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t f = f0 + u * kThreads;
-    if (f < a.end_vec) *reinterpret_cast<vec16*>(y + f * 16) = buf[u];
+    if (f < a.end_vec) store16(y + f * 16, buf[u]);
   }
 }
 
@@ -179,12 +188,12 @@ __global__ __launch_bounds__(kThreads) void gather_unpad_kernel(GatherArgs a) {
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t f = f0 + u * kThreads;
-    if (f < nvec) buf[u] = *reinterpret_cast<const vec16*>(src + f * 16);
+    if (f < nvec) buf[u] = load16(src + f * 16);
   }
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const int64_t f = f0 + u * kThreads;
-    if (f < nvec) *reinterpret_cast<vec16*>(dst + f * 16) = buf[u];
+    if (f < nvec) store16(dst + f * 16, buf[u]);
   }
 }
 
