@@ -116,8 +116,10 @@ __device__ __forceinline__ TileCoord decode_tile(const AttnArgs& a) {
   return t;
 }
 
+// max of x over the lane pair (l, l ^ 32): one v_permlane32_swap (no LDS trip)
 __device__ __forceinline__ float wave_max_pair(float x) {
-  return fmaxf(x, __shfl_xor(x, 32));
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
 // ---------------------------------------------------------------- bf16 kernel
@@ -293,9 +295,13 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   const int k_base = T::offset(l32, h);
   const int v_base = T::offset(4 * h + (s16 >> 2), 2 * dh + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
 
-  // One key tile on LDS buffers (kb_, vb_), in parts of 32 keys: QK^T of the
-  // part, the online-softmax update, then PV.
+  // One key tile on LDS buffers (kb_, vb_), in parts of 32 keys, software
+  // pipelined inside the wave: for part k the program issues PV(k-1), checks
+  // the running max against S(k) (the only branch), then issues the QK^T
+  // MFMAs of part k+1 while computing the exponentials of part k, so the MFMA
+  // unit has independent work while the VALU runs the softmax.
   auto compute = [&](int kt, const char* kb_, const char* vb_) __attribute__((always_inline)) {
+    constexpr int NP = KT / 32;   // parts per tile
     const int64_t key0 = int64_t(kt) * KT;
     const uint8_t cls = tile_class(kt);
     const bool edge = (MASK && cls == kTilePartial) || key0 + KT > a.kv_end;
@@ -310,14 +316,12 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][ct] : 0ull;
         }
     }
+    // S^T of part kb (keys x queries).  The K fragment (key 32*kb + l32,
+    // chunk 2*ks + h) feeds every query block.  Lane (l32, h), register v then
+    // holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
+    auto qk = [&](int kb, f32x16 (&sx)[QB]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kb = 0; kb < KT / 32; ++kb) {
-      // S^T of the part (keys x queries).  The K fragment (key 32*kb + l32,
-      // chunk 2*ks + h) feeds every query block.  Lane (l32, h), register v
-      // then holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
-      f32x16 s[QB];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) s[qb] = f32x16{};
+      for (int qb = 0; qb < QB; ++qb) sx[qb] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < NKS; ++ks) {
         // offset(32*kb + l32, 2*ks + h) - offset(l32, h) is lane-independent
@@ -325,60 +329,15 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
             kb_ + k_base + (T::offset(32 * kb, 2 * ks) - T::offset(0, 0)));
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], s[qb], 0, 0, 0);
+          sx[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sx[qb], 0, 0, 0);
       }
-      if (edge) {
-        // visible iff key < kv_end (and its mask bit is set on partial tiles)
-        const int room = int(a.kv_end - key0) - 4 * h - 32 * kb;
-#pragma unroll
-        for (int qb = 0; qb < QB; ++qb) {
-          // bit 8*(v/4) + v%4 of wsh is register v's key
-          const uint32_t wsh = MASK ? uint32_t(mw[qb][kb / 2] >> (32 * (kb & 1) + 4 * h)) : 0u;
-#pragma unroll
-          for (int v = 0; v < 16; ++v) {
-            const int kofs = 8 * (v >> 2) + (v & 3);
-            bool vis = kofs < room;
-            if (MASK && cls == kTilePartial) vis = vis && ((wsh >> kofs) & 1u);
-            if (!vis) s[qb][v] = -INFINITY;
-          }
-        }
-      }
-      // softmax numerators, rounded to bf16: the B operands of the PV MFMA
-      bf16x8 pf[QB][2];
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
-#pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[qb][v]);
-        const float mxc = wave_max_pair(mx) * a.c;
-        if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run[qb], mxc);
-          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
-          l_run[qb] *= alpha;
-#pragma unroll
-          for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
-          m_run[qb] = m_new;
-        }
-        const float nm = -m_run[qb];
-        float part = 0.f;
-#pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            pf[qb][j2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s[qb][8 * j2 + e], a.c, nm)));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pair = {pf[qb][j2][e], pf[qb][j2][e + 1]};
-            part = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part, false);
-          }
-        }
-        l_run[qb] += part;
-      }
-      // O^T += V^T P^T.  B element e of lane half h is key 16*j2 + 8*(e/4) + 4*h + e%4
-      // of the part.  The V^T operand takes the same keys through two transpose
-      // reads: in each 16-lane group, source lane s addresses key k0 + s/4 at dims
-      // n0 + 4*(s%4) .. +3, and lane j receives dim n0 + j of keys k0 .. k0+3
-      // (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
+    };
+    // O^T += V^T P^T for part kb.  B element e of lane half h is key
+    // 16*j2 + 8*(e/4) + 4*h + e%4 of the part.  The V^T operand takes the same
+    // keys through two transpose reads: in each 16-lane group, source lane s
+    // addresses key k0 + s/4 at dims n0 + 4*(s%4) .. +3, and lane j receives
+    // dim n0 + j of keys k0 .. k0+3 (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
+    auto pv = [&](int kb, const bf16x8 (&px)[QB][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
 #pragma unroll
@@ -391,10 +350,76 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
 #pragma unroll
           for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, pf[qb][j2], oacc[qb][d], 0, 0, 0);
+            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, px[qb][j2], oacc[qb][d], 0, 0, 0);
         }
       }
+    };
+
+    f32x16 s_cur[QB], s_nxt[QB];
+    bf16x8 p_prev[QB][2];
+    qk(0, s_cur);
+#pragma unroll
+    for (int kb = 0; kb < NP; ++kb) {
+      if (kb > 0) pv(kb - 1, p_prev);
+      if (edge) {
+        // visible iff key < kv_end (and its mask bit is set on partial tiles)
+        const int room = int(a.kv_end - key0) - 4 * h - 32 * kb;
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) {
+          // bit 8*(v/4) + v%4 of wsh is register v's key
+          const uint32_t wsh = MASK ? uint32_t(mw[qb][kb / 2] >> (32 * (kb & 1) + 4 * h)) : 0u;
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int kofs = 8 * (v >> 2) + (v & 3);
+            bool vis = kofs < room;
+            if (MASK && cls == kTilePartial) vis = vis && ((wsh >> kofs) & 1u);
+            if (!vis) s_cur[qb][v] = -INFINITY;
+          }
+        }
+      }
+      // running max: raise it (and rescale what is accumulated) only when this
+      // part's max exceeds it by more than the slack
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        float mx = -INFINITY;
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[qb][v]);
+        const float mxc = wave_max_pair(mx) * a.c;
+        if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
+          const float m_new = fmaxf(m_run[qb], mxc);
+          const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
+          l_run[qb] *= alpha;
+#pragma unroll
+          for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
+          m_run[qb] = m_new;
+        }
+      }
+      if (kb + 1 < NP) qk(kb + 1, s_nxt);
+      // softmax numerators of part kb, rounded to bf16: the B operands of PV
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) {
+        const float nm = -m_run[qb];
+        float part = 0.f;
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            p_prev[qb][j2][e] =
+                static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][8 * j2 + e], a.c, nm)));
+#pragma unroll
+          for (int e = 0; e < 8; e += 2) {
+            const bf16x2 pair = {p_prev[qb][j2][e], p_prev[qb][j2][e + 1]};
+            part = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part, false);
+          }
+        }
+        l_run[qb] += part;
+      }
+      if (kb + 1 < NP) {
+#pragma unroll
+        for (int qb = 0; qb < QB; ++qb) s_cur[qb] = s_nxt[qb];
+      }
     }
+    pv(NP - 1, p_prev);
   };
 
   // NBUF-stage pipeline over the tiles, unrolled by NBUF so that every LDS
