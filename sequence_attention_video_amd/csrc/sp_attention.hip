@@ -54,7 +54,8 @@ constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a 
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
 constexpr int BF16_WAVES = BM / (32 * QB);
 constexpr int BF16_THREADS = 64 * BF16_WAVES;
-constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales
+constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
+constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
 
@@ -355,6 +356,24 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
       }
     };
 
+    // p = 2^(c*s - m) for the 32 keys of one lane pair's part, as bf16 B
+    // operands; returns this lane's sum of the rounded p (v_dot2 with ones)
+    auto exp_part = [&](const f32x16& sx, float m, bf16x8 (&px)[2]) __attribute__((always_inline)) -> float {
+      const float nm = -m;
+      float sum = 0.f;
+#pragma unroll
+      for (int j2 = 0; j2 < 2; ++j2) {
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          px[j2][e] = static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(sx[8 * j2 + e], a.c, nm)));
+#pragma unroll
+        for (int e = 0; e < 8; e += 2) {
+          const bf16x2 pair = {px[j2][e], px[j2][e + 1]};
+          sum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, sum, false);
+        }
+      }
+      return sum;
+    };
     f32x16 s_cur[QB], s_nxt[QB];
     bf16x8 p_prev[QB][2];
     qk(0, s_cur);
@@ -377,40 +396,27 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           }
         }
       }
-      // running max: raise it (and rescale what is accumulated) only when this
-      // part's max exceeds it by more than the slack
+      if (kb + 1 < NP) qk(kb + 1, s_nxt);
+      // softmax numerators of part kb against the running max, rounded to bf16
+      // (the B operands of PV).  Every p is <= this lane's sum of the part, so a
+      // sum <= kSumLimit proves that no p exceeds it and the running max may
+      // stay; otherwise (rare: the first visible keys of a row, or a score far
+      // above the running max) raise the max to the part's, rescale what is
+      // accumulated, and recompute.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float mx = -INFINITY;
+        float part = exp_part(s_cur[qb], m_run[qb], p_prev[qb]);
+        if (__ballot(!(part <= kSumLimit)) != 0) {
+          float mx = -INFINITY;
 #pragma unroll
-        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[qb][v]);
-        const float mxc = wave_max_pair(mx) * a.c;
-        if (__ballot(mxc > m_run[qb] + kRescaleSlack) != 0) {
-          const float m_new = fmaxf(m_run[qb], mxc);
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[qb][v]);
+          const float m_new = fmaxf(m_run[qb], wave_max_pair(mx) * a.c);
           const float alpha = __builtin_amdgcn_exp2f(m_run[qb] - m_new);
           l_run[qb] *= alpha;
 #pragma unroll
           for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
           m_run[qb] = m_new;
-        }
-      }
-      if (kb + 1 < NP) qk(kb + 1, s_nxt);
-      // softmax numerators of part kb, rounded to bf16: the B operands of PV
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb) {
-        const float nm = -m_run[qb];
-        float part = 0.f;
-#pragma unroll
-        for (int j2 = 0; j2 < 2; ++j2) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e)
-            p_prev[qb][j2][e] =
-                static_cast<__bf16>(__builtin_amdgcn_exp2f(__builtin_fmaf(s_cur[qb][8 * j2 + e], a.c, nm)));
-#pragma unroll
-          for (int e = 0; e < 8; e += 2) {
-            const bf16x2 pair = {p_prev[qb][j2][e], p_prev[qb][j2][e + 1]};
-            part = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, part, false);
-          }
+          part = exp_part(s_cur[qb], m_run[qb], p_prev[qb]);
         }
         l_run[qb] += part;
       }
