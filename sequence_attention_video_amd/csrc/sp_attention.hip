@@ -46,14 +46,15 @@
 namespace sp {
 namespace {
 
-constexpr int BM = 256;              // query rows per bf16 workgroup, and the mask-class tile height
+constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
+constexpr int BF16_WAVES = 8;        // waves per bf16 workgroup
+constexpr int BF16_THREADS = 64 * BF16_WAVES;
+constexpr int BM = 32 * QB * BF16_WAVES;   // query rows per bf16 workgroup, and the mask-class tile height
 constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
-constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
 constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
-constexpr int BF16_WAVES = BM / (32 * QB);
-constexpr int BF16_THREADS = 64 * BF16_WAVES;
+static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
@@ -144,13 +145,12 @@ template <int D>
 struct Bf16Tile {
   static constexpr int KPG = 512 / D;               // keys per 1 KiB group
   static constexpr int NG = KT / KPG;               // groups per tile = direct loads per tile
-  static constexpr int NLD = NG / BF16_WAVES;       // direct loads per wave per tile and tensor
+  static constexpr int NLD = (NG + BF16_WAVES - 1) / BF16_WAVES;   // direct loads per wave per tile and tensor (at most)
   static constexpr int GROUP_BYTES = 1024 + 64;
   static constexpr int TILE_BYTES = NG * GROUP_BYTES;
   static constexpr int NKS = D / 16;                // k-steps of QK^T
   static constexpr int NDB = D / 32;                // 32-row blocks of O^T
   static_assert(D == 64 || D == 128, "bf16 tiles are built for D = 64 and 128");
-  static_assert(NG % BF16_WAVES == 0, "every wave issues the same number of direct loads");
   static_assert(2 * NBUF * TILE_BYTES <= 160 * 1024, "K and V buffers must fit the 160 KiB LDS");
 
   static __host__ __device__ constexpr int pos(int n, int c) {
@@ -172,7 +172,7 @@ __device__ __forceinline__ void wait_vmem() {
 template <int D, bool MASK>
 __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   using T = Bf16Tile<D>;
-  constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD;
+  constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD, NG = T::NG;
   constexpr int LOADS = 2 * NLD;   // direct loads per wave per tile (K and V)
   // Each buffer is its own LDS object, so that the compiler can tell which
   // buffer a direct load writes and never waits on it before reading another.
@@ -258,7 +258,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     return kt;
   };
 
-  // Direct loads: per tile and tensor, wave w fills groups w*NLD .. w*NLD+NLD-1.
+  // Direct loads: per tile and tensor, wave w fills groups w, w + WAVES, ...
   // Lane i of a load writes LDS byte 16*i of its group, which holds chunk
   // c = i / KPG of the key whose pos() is i % KPG.  Keys past kv_end read row
   // kv_end-1 instead (in bounds and finite); their scores are masked to -inf,
@@ -273,7 +273,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     if (key0 + KT <= a.kv_end) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int grp = wu * NLD + j;
+        const int grp = j * BF16_WAVES + wu;
+        if (NG % BF16_WAVES != 0 && grp >= NG) break;
         const int64_t row = key0 + grp * KPG;
         __builtin_amdgcn_global_load_lds(kp + row * a.ks[2] + k_lane, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
         __builtin_amdgcn_global_load_lds(vp + row * a.vs[2] + v_lane, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, 0, 0);
@@ -281,7 +282,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int grp = wu * NLD + j;
+        const int grp = j * BF16_WAVES + wu;
+        if (NG % BF16_WAVES != 0 && grp >= NG) break;
         int64_t key = key0 + grp * KPG + ld_n;
         if (key >= a.kv_end) key = a.kv_end - 1;
         __builtin_amdgcn_global_load_lds(kp + key * a.ks[2] + 8 * ld_c, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
@@ -297,10 +299,10 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   const int v_base = T::offset(4 * h + (s16 >> 2), 2 * dh + ((s16 & 3) >> 1)) + 8 * (s16 & 1);
 
   // One key tile on LDS buffers (kb_, vb_), in parts of 32 keys, software
-  // pipelined inside the wave: for part k the program issues PV(k-1), checks
-  // the running max against S(k) (the only branch), then issues the QK^T
-  // MFMAs of part k+1 while computing the exponentials of part k, so the MFMA
-  // unit has independent work while the VALU runs the softmax.
+  // pipelined inside the wave: for part k the program issues PV(k-1) and the
+  // QK^T MFMAs of part k+1 while computing the exponentials of part k, so the
+  // MFMA unit has independent work while the VALU runs the softmax; the rare
+  // rescale branch comes after.
   auto compute = [&](int kt, const char* kb_, const char* vb_) __attribute__((always_inline)) {
     constexpr int NP = KT / 32;   // parts per tile
     const int64_t key0 = int64_t(kt) * KT;
@@ -375,11 +377,10 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
       return sum;
     };
     f32x16 s_cur[QB], s_nxt[QB];
-    bf16x8 p_prev[QB][2];
+    bf16x8 p_prev[QB][2], p_cur[QB][2];
     qk(0, s_cur);
 #pragma unroll
     for (int kb = 0; kb < NP; ++kb) {
-      if (kb > 0) pv(kb - 1, p_prev);
       if (edge) {
         // visible iff key < kv_end (and its mask bit is set on partial tiles)
         const int room = int(a.kv_end - key0) - 4 * h - 32 * kb;
@@ -396,17 +397,23 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           }
         }
       }
+      // One basic block for the scheduler: PV of the previous part and QK^T of
+      // the next part (independent MFMA chains) around the exponentials of this
+      // part.  p of this part is computed against the running max and rounded
+      // to bf16 (the B operands of PV).
+      if (kb > 0) pv(kb - 1, p_prev);
       if (kb + 1 < NP) qk(kb + 1, s_nxt);
-      // softmax numerators of part kb against the running max, rounded to bf16
-      // (the B operands of PV).  Every p is <= this lane's sum of the part, so a
-      // sum <= kSumLimit proves that no p exceeds it and the running max may
-      // stay; otherwise (rare: the first visible keys of a row, or a score far
-      // above the running max) raise the max to the part's, rescale what is
-      // accumulated, and recompute.
+      float part[QB];
+#pragma unroll
+      for (int qb = 0; qb < QB; ++qb) part[qb] = exp_part(s_cur[qb], m_run[qb], p_cur[qb]);
+      // Every p is <= this lane's sum of the part, so a sum <= kSumLimit proves
+      // that no p exceeds it and the running max may stay; otherwise (rare: the
+      // first visible keys of a row, or a score far above the running max) raise
+      // the max to the part's, rescale what is accumulated (which includes
+      // PV of the previous part, issued above), and recompute.
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) {
-        float part = exp_part(s_cur[qb], m_run[qb], p_prev[qb]);
-        if (__ballot(!(part <= kSumLimit)) != 0) {
+        if (__ballot(!(part[qb] <= kSumLimit)) != 0) {
           float mx = -INFINITY;
 #pragma unroll
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s_cur[qb][v]);
@@ -416,13 +423,12 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
           for (int d = 0; d < NDB; ++d) oacc[qb][d] *= alpha;
           m_run[qb] = m_new;
-          part = exp_part(s_cur[qb], m_run[qb], p_prev[qb]);
+          part[qb] = exp_part(s_cur[qb], m_run[qb], p_cur[qb]);
         }
-        l_run[qb] += part;
-      }
-      if (kb + 1 < NP) {
+        l_run[qb] += part[qb];
 #pragma unroll
-        for (int qb = 0; qb < QB; ++qb) s_cur[qb] = s_nxt[qb];
+        for (int j2 = 0; j2 < 2; ++j2) p_prev[qb][j2] = p_cur[qb][j2];
+        if (kb + 1 < NP) s_cur[qb] = s_nxt[qb];
       }
     }
     pv(NP - 1, p_prev);
@@ -636,7 +642,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- mask tiles
 
-// One workgroup per (batch, q-tile, k-tile), one mask row per thread: reads
+// One workgroup per (batch, q-tile, k-tile), mask rows spread over threads: reads
 // the row's BN bytes of the tile (as wide as their alignment allows), writes
 // them as one 64-bit visibility word (bit j = key BN*kt + j), and records
 // whether none, all, or some of the tile's in-range bytes are set.
@@ -651,16 +657,16 @@ __device__ __forceinline__ uint64_t nonzero_bytes_to_bits(uint64_t x) {
 __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
                                                                int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
                                                                uint64_t* bits) {
-  static_assert(BM == kThreads, "one mask row per thread");
   static_assert(BN == 64, "one 64-bit word per row and tile");
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int64_t row = int64_t(qt) * BM + threadIdx.x;
   const int64_t col0 = int64_t(kt) * BN;
   const int n = int(Tk - col0 < BN ? Tk - col0 : BN);           // in-range keys of the tile
   const uint64_t full = n == 64 ? ~0ull : ((1ull << n) - 1);
   int any = 0, all = 1;
-  if (row < Tq) {
+  for (int r = threadIdx.x; r < BM; r += kThreads) {
+    const int64_t row = int64_t(qt) * BM + r;
+    if (row >= Tq) break;
     const uint8_t* p = mask + b * mask_bs + row * Tk + col0;
     uint64_t word = 0;
     if (n == BN && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
@@ -673,8 +679,8 @@ __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* 
       for (int c = 0; c < n; ++c) word |= uint64_t(p[c] != 0) << c;
     }
     bits[(b * Tq + row) * int64_t(nkt) + kt] = word;
-    any = word != 0;
-    all = word == full;
+    any |= word != 0;
+    all &= word == full;
   }
   any = __syncthreads_or(any);
   all = __syncthreads_and(all);
