@@ -54,6 +54,7 @@ constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
+constexpr bool kPrefetchV = false;   // read the V operands of a part one block before its PV MFMAs
 static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
@@ -340,7 +341,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     // keys through two transpose reads: in each 16-lane group, source lane s
     // addresses key k0 + s/4 at dims n0 + 4*(s%4) .. +3, and lane j receives
     // dim n0 + j of keys k0 .. k0+3 (k0 = 32*kb + 16*j2 + 4*h (+8), n0 = 32*d + 16*dh).
-    auto pv = [&](int kb, const bf16x8 (&px)[QB][2]) __attribute__((always_inline)) {
+    auto load_v = [&](int kb, bf16x8 (&vx)[NDB][2]) __attribute__((always_inline)) {
 #pragma unroll
       for (int d = 0; d < NDB; ++d) {
 #pragma unroll
@@ -350,12 +351,23 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
           const int o1 = T::offset(32 * kb + 16 * j2 + 8, 4 * d) - z;
           const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + v_base + o0));
           const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(vb_ + v_base + o1));
-          const bf16x8 vf = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
-#pragma unroll
-          for (int qb = 0; qb < QB; ++qb)
-            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vf, px[qb][j2], oacc[qb][d], 0, 0, 0);
+          vx[d][j2] = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
         }
       }
+    };
+    auto pv_f = [&](const bf16x8 (&vx)[NDB][2], const bf16x8 (&px)[QB][2]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int d = 0; d < NDB; ++d)
+#pragma unroll
+        for (int j2 = 0; j2 < 2; ++j2)
+#pragma unroll
+          for (int qb = 0; qb < QB; ++qb)
+            oacc[qb][d] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vx[d][j2], px[qb][j2], oacc[qb][d], 0, 0, 0);
+    };
+    auto pv = [&](int kb, const bf16x8 (&px)[QB][2]) __attribute__((always_inline)) {
+      bf16x8 vx[NDB][2];
+      load_v(kb, vx);
+      pv_f(vx, px);
     };
 
     // p = 2^(c*s - m) for the 32 keys of one lane pair's part, as bf16 B
@@ -378,6 +390,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     };
     f32x16 s_cur[QB], s_nxt[QB];
     bf16x8 p_prev[QB][2], p_cur[QB][2];
+    bf16x8 v_prev[NDB][2], v_cur[NDB][2];   // V fragments one part ahead (kPrefetchV)
     qk(0, s_cur);
 #pragma unroll
     for (int kb = 0; kb < NP; ++kb) {
@@ -401,7 +414,13 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
       // the next part (independent MFMA chains) around the exponentials of this
       // part.  p of this part is computed against the running max and rounded
       // to bf16 (the B operands of PV).
-      if (kb > 0) pv(kb - 1, p_prev);
+      if constexpr (kPrefetchV) {
+        // V fragments of part kb-1 were read in the previous block
+        if (kb > 0) pv_f(v_prev, p_prev);
+        load_v(kb, v_cur);
+      } else {
+        if (kb > 0) pv(kb - 1, p_prev);
+      }
       if (kb + 1 < NP) qk(kb + 1, s_nxt);
       float part[QB];
 #pragma unroll
@@ -430,8 +449,15 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
         for (int j2 = 0; j2 < 2; ++j2) p_prev[qb][j2] = p_cur[qb][j2];
         if (kb + 1 < NP) s_cur[qb] = s_nxt[qb];
       }
+      if constexpr (kPrefetchV) {
+#pragma unroll
+        for (int d = 0; d < NDB; ++d)
+#pragma unroll
+          for (int j2 = 0; j2 < 2; ++j2) v_prev[d][j2] = v_cur[d][j2];
+      }
     }
-    pv(NP - 1, p_prev);
+    if constexpr (kPrefetchV) pv_f(v_prev, p_prev);
+    else pv(NP - 1, p_prev);
   };
 
   // NBUF-stage pipeline over the tiles, unrolled by NBUF so that every LDS
