@@ -168,8 +168,9 @@ def write_kernel_trace_summary(stats_csv: str, bench_json: str, title: str, cmd:
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first; the clocks need ~0.1 s of sustained work to settle")
     ap.add_argument("--config", default="video_self")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -416,8 +417,8 @@ def cpu_baseline(wl, x, budget_s: float):
     dt = time.perf_counter() - t0
     return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"{rows_done} query rows (batch 0; heads {heads_done[0]}..{heads_done[-1]}, rank-major) "
-                      f"against all {Tp} keys, float64 NumPy oracle, {dt:.1f} s; the full step is "
-                      f"{wl.H * wl.B} such heads",
+                      f"against all {Tp} keys, float64 NumPy oracle, {dt:.1f} s; the whole step is "
+                      f"{wl.H * wl.B} heads of {nq} query rows",
             "seconds": round(dt, 2)}
 
 
