@@ -264,31 +264,47 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // c = i / KPG of the key whose pos() is i % KPG.  Keys past kv_end read row
   // kv_end-1 instead (in bounds and finite); their scores are masked to -inf,
   // so their weight is exactly 0.
+  //
+  // The loads are MUBUF buffer loads into LDS through a descriptor based at
+  // the tile's first key (rebuilt per tile, 32-bit offsets inside it, bounds
+  // checked by the descriptor).  The FLAT-encoded global_load_lds would do
+  // the same copy, but while one of those is in flight the compiler cannot
+  // count LDS reads precisely and waits for all of them before every MFMA.
   const int ld_c = lane / KPG;
   const int ld_n = (KPG == 8 ? ((lane % KPG) ^ (4 * (ld_c & 1))) : (lane % KPG));
   const int wu = __builtin_amdgcn_readfirstlane(w);          // wave index, as a scalar
-  const int64_t k_lane = int64_t(ld_n) * a.ks[2] + 8 * ld_c;
-  const int64_t v_lane = int64_t(ld_n) * a.vs[2] + 8 * ld_c;
+  const int32_t kst = int32_t(a.ks[2]) * 2, vst = int32_t(a.vs[2]) * 2;   // token strides in bytes (host-checked)
+  const int32_t k_lane = ld_n * kst + 16 * ld_c;
+  const int32_t v_lane = ld_n * vst + 16 * ld_c;
+  const int32_t k_nrec = (KT - 1) * kst + 2 * D, v_nrec = (KT - 1) * vst + 2 * D;
+  constexpr int32_t kRsrcWord3 = 0x00020000;   // raw 32-bit data format, no swizzle
   auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
     const int64_t key0 = int64_t(kt) * KT;
+    const __amdgpu_buffer_rsrc_t krs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp + key0 * a.ks[2]), 0, k_nrec, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t vrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(vp + key0 * a.vs[2]), 0, v_nrec, kRsrcWord3);
     if (key0 + KT <= a.kv_end) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int grp = j * BF16_WAVES + wu;
         if (NG % BF16_WAVES != 0 && grp >= NG) break;
-        const int64_t row = key0 + grp * KPG;
-        __builtin_amdgcn_global_load_lds(kp + row * a.ks[2] + k_lane, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + row * a.vs[2] + v_lane, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, k_lane,
+                                                 grp * KPG * kst, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, v_lane,
+                                                 grp * KPG * vst, 0, 0);
       }
     } else {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
         const int grp = j * BF16_WAVES + wu;
         if (NG % BF16_WAVES != 0 && grp >= NG) break;
-        int64_t key = key0 + grp * KPG + ld_n;
-        if (key >= a.kv_end) key = a.kv_end - 1;
-        __builtin_amdgcn_global_load_lds(kp + key * a.ks[2] + 8 * ld_c, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(vp + key * a.vs[2] + 8 * ld_c, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, 0, 0);
+        int32_t n = grp * KPG + ld_n;                       // key - key0
+        if (key0 + n >= a.kv_end) n = int32_t(a.kv_end - 1 - key0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16,
+                                                 n * kst + 16 * ld_c, 0, 0, 0);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16,
+                                                 n * vst + 16 * ld_c, 0, 0, 0);
       }
     }
   };
@@ -800,6 +816,9 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   const int64_t nqt_cls = div_up(Tq, BM);
   const int64_t nwg = nqt * Hl * B * R;
   if (nwg >= (int64_t(1) << 31) || nkt >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  // the bf16 kernel addresses one key tile of K and of V with 32-bit byte offsets
+  if (dtype == SP_BF16 && ((KT - 1) * (ks.token > vs.token ? ks.token : vs.token) + D) * eb >= (int64_t(1) << 31))
+    return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
   const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, has_mask, mask_batch_stride);
   if (has_mask && (workspace == nullptr || workspace_bytes < need)) return SP_ERR_INVALID_ARG;
