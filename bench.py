@@ -314,6 +314,36 @@ def main():
     del sets
     torch.cuda.empty_cache()
 
+    # -- one rank's share alone (R = 1): the attention launch each GPU runs when
+    #    the W ranks are devices; few query tiles, so the library splits keys
+    share_out = torch.empty_like(step.oh[0])
+    mbs = 0
+    if step.mask is not None and step.mask_ext.shape[0] > 1:
+        mbs = step.mask_ext.stride(0)
+    tq_share = wl.Tq if wl.cross else Tp
+    need = binding.sp_masked_attention_workspace_size(1, B, tq_share, Tp, Hl, D, binding._dtype_code(step.kh),
+                                                      step.mask is not None, mbs)
+    # the mask part alone is what the (never split) fp32 kernel would need
+    mask_part = binding.sp_masked_attention_workspace_size(1, B, tq_share, Tp, Hl, D, binding.SP_F32,
+                                                           step.mask is not None, mbs)
+    share_split = wl.dtype == "bf16" and need > mask_part
+    share_ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
+    n_share = 5 if attn_flops > 4e12 else 50
+    for _ in range(n_share):
+        step.attention_rank(0, share_out, share_ws)
+    s0 = torch.cuda.Event(enable_timing=True)
+    s1 = torch.cuda.Event(enable_timing=True)
+    s0.record(stream)
+    for _ in range(n_share):
+        step.attention_rank(0, share_out, share_ws)
+    s1.record(stream)
+    torch.cuda.synchronize()
+    ms_share = s0.elapsed_time(s1) / n_share
+    share_diff = float((share_out.float() - step.oh[0].float()).abs().max().item())
+    share_flops = attn_flops // W
+    share_tflops = share_flops / (ms_share * 1e-3) / 1e12
+    del share_ws
+
     # -- oracle-free sanity on the timed buffers (parity proper lives in tests/)
     finite = bool(torch.isfinite(step.out.float()).all().item())
     back = torch.empty_like(step.kp)
@@ -342,6 +372,10 @@ def main():
                          "GB/s": round(gbs(relayout_o_bytes, ms_gh), 1)},
         "gather_output_tokens": {"ms": round(ms_gather, 4), "bytes": gather_bytes,
                                  "GB/s": round(gbs(gather_bytes, ms_gather), 1)},
+        "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),
+                                        "mfma_frac": round(share_tflops / peak_mfma, 4), "R": 1,
+                                        "split": share_split,
+                                        "max_abs_diff_vs_all_ranks": share_diff},
     }
 
     cpu = None

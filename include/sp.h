@@ -142,13 +142,20 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * mask_batch_stride (0 = one mask for every batch), or NULL for the key-only
  * padding mask.  The mask is shared by every rank and head.
  * workspace: device scratch of sp_masked_attention_workspace_size() bytes,
- * 256-byte aligned (per-tile mask classes and bit-packed mask rows, rewritten
- * by every call); may be NULL when that size is 0.
+ * 256-byte aligned, rewritten by every call; may be NULL when that size is 0.
+ * With a mask it holds per-tile mask classes and bit-packed mask rows and is
+ * required.  Without a mask (bf16 only) it holds the float32 partial results
+ * of a split launch: when the query tiles are too few to fill the GPU (one
+ * rank's share of a few heads), the key range of every tile is spread over
+ * all compute units and a second kernel merges the partial results.  Without
+ * it (NULL or smaller) the same call runs unsplit: same result up to float32
+ * summation order, slower on such shapes.
  * Supported: SP_BF16 with D in {64, 128} (bf16 MFMA, float32 softmax and
  * accumulation, output rounded to nearest even) and SP_F32 with D in
  * {16, 64, 128} (float32 MFMA throughout).
- * Errors: sizes < 0, null tensors, kv_valid_len < 0, workspace too small ->
- * SP_ERR_INVALID_ARG; other D -> SP_ERR_UNSUPPORTED.
+ * Errors: sizes < 0, null tensors, kv_valid_len < 0, a mask without a large
+ * enough workspace -> SP_ERR_INVALID_ARG; other D, or (bf16) a K or V token
+ * stride above 8 million elements (its 32-bit tile offsets) -> SP_ERR_UNSUPPORTED.
  */
 size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
                                           sp_dtype dtype, int32_t has_mask, int64_t mask_batch_stride);

@@ -57,6 +57,7 @@ constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pip
 constexpr bool kPrefetchV = false;   // read the V operands of a part one block before its PV MFMAs
 static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
+constexpr int kSumChains = 1;         // independent accumulators of a part's row sum
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
@@ -64,6 +65,7 @@ enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
@@ -88,6 +90,11 @@ struct AttnArgs {
   int32_t nqt_cls;                       // query tiles of the class map (height BM)
   float c;                               // scale * log2(e)
   uint32_t nwg;
+  // split launches (bf16, no user mask): the key tiles of all items in order
+  int64_t units;                         // items * nku
+  int64_t upw;                           // units per workgroup (< nku)
+  int32_t nku;                           // key tiles of KT per item
+  float* part;                           // partial records, two per workgroup
 };
 
 // Workgroup i runs on XCD i % 8.  Give XCD x a contiguous range of logical
@@ -103,9 +110,10 @@ struct TileCoord {
   int32_t head, qt;
 };
 
+// Item i (one query tile of one (rank, batch, head)): query tile fastest,
+// then head, batch, rank.
 template <bool MASK>
-__device__ __forceinline__ TileCoord decode_tile(const AttnArgs& a) {
-  uint32_t rest = xcd_remap(blockIdx.x, a.nwg);
+__device__ __forceinline__ TileCoord decode_item(const AttnArgs& a, uint32_t rest) {
   TileCoord t;
   const uint32_t qi = rest % uint32_t(a.nqt);
   rest /= uint32_t(a.nqt);
@@ -170,7 +178,7 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, bool MASK>
+template <int D, bool MASK, bool SPLIT>
 __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   using T = Bf16Tile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD, NG = T::NG;
@@ -193,9 +201,33 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   };
   using I0 = std::integral_constant<int, 0>;
 
-  const TileCoord tc = decode_tile<MASK>(a);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
+
+  // Work split.  Without SPLIT a workgroup runs one item over all of its key
+  // tiles.  With SPLIT (launches whose items cannot fill the GPU) the key
+  // tiles of all items, item after item, form one sequence of units, and
+  // logical workgroup g runs units [g*upw, (g+1)*upw).  As upw < nku that is at
+  // most two segments of at most two items; each segment ends in a partial
+  // record (unnormalised O rows, running max and sum) in slot 2*g + segment,
+  // which attn_combine_kernel merges into O.
+  const uint32_t gl = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0u;
+  int64_t u_next = SPLIT ? int64_t(gl) * a.upw : 0;
+  const int64_t u_end = SPLIT ? (a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
+  for (int seg = 0;; ++seg) {
+  uint32_t item;
+  int kt_first = 0, kt_stop = 0;
+  if constexpr (SPLIT) {
+    if (u_next >= u_end) break;
+    item = uint32_t(u_next / a.nku);
+    kt_first = int(u_next - int64_t(item) * a.nku);
+    kt_stop = int(a.nku - kt_first < u_end - u_next ? a.nku : kt_first + (u_end - u_next));
+    u_next += kt_stop - kt_first;
+    if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
+  } else {
+    item = xcd_remap(blockIdx.x, a.nwg);
+  }
+  const TileCoord tc = decode_item<MASK>(a, item);
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
@@ -238,8 +270,9 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + (bm * a.Tq + (qvalid[qb] ? qrow[qb] : 0)) * int64_t(a.nkt);
   }
   // Key tiles of KT keys; with a user mask a tile's class combines the classes
-  // of its BN-key class tiles, and empty tiles are skipped.
-  const int nkt_eff = int((a.kv_end + KT - 1) / KT);
+  // of its BN-key class tiles, and empty tiles are skipped.  This segment runs
+  // tiles [kt_first, nkt_eff).
+  const int nkt_eff = SPLIT ? kt_stop : int((a.kv_end + KT - 1) / KT);
   auto tile_class = [&](int kt) __attribute__((always_inline)) -> uint8_t {
     if (!MASK) return kTileFull;
     bool any = false, all = true;
@@ -390,7 +423,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     // operands; returns this lane's sum of the rounded p (v_dot2 with ones)
     auto exp_part = [&](const f32x16& sx, float m, bf16x8 (&px)[2]) __attribute__((always_inline)) -> float {
       const float nm = -m;
-      float sum = 0.f;
+      // kSumChains independent dot2 accumulators, so the sum is not one serial chain
+      float sums[kSumChains] = {};
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
@@ -399,10 +433,13 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pair = {px[j2][e], px[j2][e + 1]};
-          sum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, sum, false);
+          float& acc = sums[(4 * j2 + e / 2) % kSumChains];
+          acc = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
         }
       }
-      return sum;
+#pragma unroll
+      for (int c = 1; c < kSumChains; ++c) sums[0] += sums[c];
+      return sums[0];
     };
     f32x16 s_cur[QB], s_nxt[QB];
     bf16x8 p_prev[QB][2], p_cur[QB][2];
@@ -483,7 +520,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // every wave done with tile i-1), issue tile i+NBUF-1 into tile i-1's
   // buffer, compute tile i.
   int ahead[NBUF];   // tiles i .. i+NBUF-1
-  ahead[0] = MASK ? next_tile(-1) : 0;
+  ahead[0] = MASK ? next_tile(kt_first - 1) : kt_first;
 #pragma unroll
   for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff);
   if (ahead[0] < nkt_eff) issue(ahead[0], kbuf(I0{}), vbuf(I0{}));
@@ -521,20 +558,88 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    const float inv = lt > 0.f ? 1.0f / lt : 0.f;
-    if (qvalid[qb]) {
-      uint16_t* orow = op + qrow[qb] * a.os[2];
+    if constexpr (SPLIT) {
+      // partial record: O rows (fp32, unnormalised), then m and l per row
+      const int row = 32 * QB * w + 32 * qb + l32;
+      float* rec = a.part + int64_t(2 * gl + seg) * (BM * (D + 2));
+      if (qvalid[qb]) {
 #pragma unroll
-      for (int d = 0; d < NDB; ++d) {
+        for (int d = 0; d < NDB; ++d)
 #pragma unroll
-        for (int g4 = 0; g4 < 4; ++g4) {
-          bf16x4 ov;
+          for (int g4 = 0; g4 < 4; ++g4) {
+            const f32x4 ov = {oacc[qb][d][4 * g4], oacc[qb][d][4 * g4 + 1], oacc[qb][d][4 * g4 + 2],
+                              oacc[qb][d][4 * g4 + 3]};
+            *reinterpret_cast<f32x4*>(rec + row * D + 32 * d + 8 * g4 + 4 * h) = ov;
+          }
+        if (h == 0) {
+          rec[BM * D + row] = m_run[qb];
+          rec[BM * D + BM + row] = lt;
+        }
+      }
+    } else {
+      const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+      if (qvalid[qb]) {
+        uint16_t* orow = op + qrow[qb] * a.os[2];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[qb][d][4 * g4 + i] * inv);
-          *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * h) = ov;
+        for (int d = 0; d < NDB; ++d) {
+#pragma unroll
+          for (int g4 = 0; g4 < 4; ++g4) {
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[qb][d][4 * g4 + i] * inv);
+            *reinterpret_cast<bf16x4*>(orow + 32 * d + 8 * g4 + 4 * h) = ov;
+          }
         }
       }
     }
+  }
+  if constexpr (!SPLIT) break;
+  }   // segments
+}
+
+// Merges the partial records of split launches: for every row of every item,
+// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (the
+// same algebra as the running rescale, applied once), 0 where no key was
+// visible.  One workgroup per (item, 64 rows); 4 threads per row.
+template <int D, bool MASK>
+__global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
+  constexpr int DPT = D / 4;   // dims per thread
+  const uint32_t item = blockIdx.x;
+  const int row = blockIdx.y * 64 + (threadIdx.x >> 2);
+  const int d0 = (threadIdx.x & 3) * DPT;
+  const TileCoord tc = decode_item<MASK>(a, item);
+  const int64_t qrow = int64_t(tc.qt) * BM + row;
+  if (qrow >= a.Tq) return;
+  // workgroups whose unit ranges meet this item, and the slot of each
+  const int64_t u0 = int64_t(item) * a.nku, u1 = u0 + a.nku;   // this item's units
+  const int64_t g_first = u0 / a.upw, g_last = (u1 - 1) / a.upw;
+  float mx = -INFINITY;
+  for (int64_t g = g_first; g <= g_last; ++g) {
+    const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
+    mx = fmaxf(mx, a.part[slot * (BM * (D + 2)) + BM * D + row]);
+  }
+  float acc[DPT] = {};
+  float lsum = 0.f;
+  for (int64_t g = g_first; g <= g_last; ++g) {
+    const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
+    const float* rec = a.part + slot * (BM * (D + 2));
+    const float wgt = __builtin_amdgcn_exp2f(rec[BM * D + row] - mx);
+    lsum += wgt * rec[BM * D + BM + row];
+#pragma unroll
+    for (int i = 0; i < DPT; i += 4) {
+      const f32x4 ov = *reinterpret_cast<const f32x4*>(rec + row * D + d0 + i);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc[i + j] += wgt * ov[j];
+    }
+  }
+  const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3] + qrow * a.os[2];
+#pragma unroll
+  for (int i = 0; i < DPT; i += 4) {
+    bf16x4 ov;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) ov[j] = static_cast<__bf16>(acc[i + j] * inv);
+    *reinterpret_cast<bf16x4*>(orow + d0 + i) = ov;
   }
 }
 
@@ -551,7 +656,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   __shared__ float k_lds[BN * KST];
   __shared__ float v_lds[BN * VST];
 
-  const TileCoord tc = decode_tile<MASK>(a);
+  const TileCoord tc = decode_item<MASK>(a, xcd_remap(blockIdx.x, a.nwg));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
 
@@ -751,7 +856,15 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 template <int D, bool MASK>
 void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
   if (dt == SP_BF16) {
-    if constexpr (D % 32 == 0) hipLaunchKernelGGL((attn_bf16_kernel<D, MASK>), dim3(a.nwg), dim3(BF16_THREADS), 0, s, a);
+    if constexpr (D % 32 == 0) {
+      if (a.part) {
+        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
+                           dim3(BF16_THREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, BM / 64), dim3(kThreads), 0, s, a);
+      } else {
+        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(BF16_THREADS), 0, s, a);
+      }
+    }
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
   }
@@ -776,16 +889,62 @@ sp_status dispatch_d(int D, const AttnArgs& a, sp_dtype dt, hipStream_t s) {
 
 using namespace sp;
 
-extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
-                                                     int32_t D, sp_dtype dtype, int32_t has_mask,
-                                                     int64_t mask_batch_stride) {
-  (void)R; (void)Hl; (void)D; (void)dtype;
-  if (!has_mask || B <= 0 || Tq <= 0 || Tk <= 0) return 0;
+// Compute units of the current device (256 on MI355X; also the default when no
+// device can be queried).
+int64_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0) {
+    (void)hipGetLastError();
+    return 256;
+  }
+  return n;
+}
+
+// Split decision for the bf16 kernel without a user mask (one workgroup per CU
+// fits in LDS): with `items` query tiles of nku key tiles each, a plain launch
+// takes ceil(items / ncu) * nku tile-times; a split launch takes upw =
+// ceil(items * nku / ncu) plus about four for writing the partial records and
+// the merge launch (measured on MI355X: 3-4 us per tile-time at D = 128, about
+// 20 us for the records of a 4-head, 6144-token share).  Returns upw when the
+// split pays by 1.3x, else 0.
+int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu) {
+  if (items <= 0 || nku < 2 || ncu <= 0) return 0;
+  const int64_t upw = div_up(items * nku, ncu);
+  if (upw >= nku) return 0;
+  const int64_t plain = div_up(items, ncu) * nku;
+  return plain * 10 >= (upw + 4) * 13 ? upw : 0;
+}
+
+// bytes of partial records of a split launch: two slots per workgroup
+int64_t split_bytes(int64_t ncu, int32_t D) { return 2 * ncu * BM * (int64_t(D) + 2) * 4; }
+
+// Bytes of the mask part of the workspace (class bytes, then 256-byte aligned
+// visibility words); 0 without a mask.
+int64_t mask_ws_bytes(int64_t B, int64_t Tq, int64_t Tk, bool has_mask, int64_t mask_batch_stride) {
+  if (!has_mask) return 0;
   const int64_t bm = mask_batch_stride ? B : 1;
   // one class byte per BM x BN tile, then (256-byte aligned) one 64-bit
   // visibility word per mask row and BN-key tile
   const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
-  return size_t(cls_bytes + bm * Tq * div_up(Tk, BN) * 8);
+  return cls_bytes + bm * Tq * div_up(Tk, BN) * 8;
+}
+
+extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
+                                                     int32_t D, sp_dtype dtype, int32_t has_mask,
+                                                     int64_t mask_batch_stride) {
+  if (R <= 0 || B <= 0 || Tq <= 0 || Tk <= 0 || Hl <= 0) return 0;
+  // [mask classes and words][partial records of a split launch, 256-byte
+  // aligned]; the split part is sized for kv_valid_len = Tk (a shorter key
+  // range needs no more)
+  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask != 0, mask_batch_stride);
+  int64_t split = 0;
+  if (dtype == SP_BF16 && (D == 64 || D == 128)) {
+    const int64_t ncu = device_cus();
+    const int64_t items = div_up(Tq, BM) * Hl * B * R;
+    if (split_units_per_wg(items, div_up(Tk, KT), ncu)) split = split_bytes(ncu, D);
+  }
+  return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
 }
 
 extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
@@ -820,8 +979,8 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (dtype == SP_BF16 && ((KT - 1) * (ks.token > vs.token ? ks.token : vs.token) + D) * eb >= (int64_t(1) << 31))
     return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
-  const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, has_mask, mask_batch_stride);
-  if (has_mask && (workspace == nullptr || workspace_bytes < need)) return SP_ERR_INVALID_ARG;
+  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride);
+  if (has_mask && (workspace == nullptr || workspace_bytes < size_t(mask_bytes))) return SP_ERR_INVALID_ARG;
   if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
   if (has_mask && (B > 65535 || nqt_cls > 65535)) return SP_ERR_UNSUPPORTED;
 
@@ -844,6 +1003,21 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
   a.c = scale * 1.4426950408889634f;
   a.nwg = uint32_t(nwg);
+  a.units = 0; a.upw = 0; a.nku = 0; a.part = nullptr;
+  if (dtype == SP_BF16) {
+    const int64_t ncu = device_cus();
+    const int64_t nku = div_up(a.kv_end, KT);
+    const int64_t upw = split_units_per_wg(nwg, nku, ncu);
+    // the split runs only with room for its partial records after the mask
+    // part (as sized by sp_masked_attention_workspace_size); otherwise the
+    // plain launch runs
+    const int64_t part_at = (mask_bytes + 255) / 256 * 256;
+    if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, D)) &&
+        (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
+      a.units = nwg * nku; a.upw = upw; a.nku = int32_t(nku);
+      a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_at);
+    }
+  }
   hipStream_t s = as_stream(stream);
   if (has_mask) {
     const int64_t bm = mask_batch_stride ? B : 1;

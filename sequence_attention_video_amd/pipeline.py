@@ -125,6 +125,31 @@ class UlyssesStep:
                                    head_side, head_side, head_side, head_side, kv_valid_len=wl.T,
                                    scale=self.scale)
 
+    def attention_rank(self, r: int, out, workspace=None):
+        """Rank r's share alone (R = 1): the attention launch one GPU runs when
+        the ranks are real devices.  out: (B, Tq, Hl, D) head-side buffer.  A
+        share has few query tiles, so without a user mask the library splits
+        the key range over the GPU (workspace from the size query, allocated
+        here when not given)."""
+        wl = self.wl
+        B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
+        head_side = (B * Tp * Hl * D, Tp * Hl * D, Hl * D, D)
+        if wl.cross:
+            Tq = wl.Tq
+            qs = (Hl * D, Tq * H * D, H * D, D)
+            os_ = (B * Tq * Hl * D, Tq * Hl * D, Hl * D, D)
+            q = self.q[:, :, r * Hl:(r + 1) * Hl]
+            sp.sp_masked_attention(q, self.kh[r], self.vh[r], out, 1, B, Tq, Tp, Hl, D, qs, head_side, head_side,
+                                   os_, kv_valid_len=wl.T, scale=self.scale, workspace=workspace)
+        elif self.mask is not None:
+            sp.sp_masked_attention(self.qh[r], self.kh[r], self.vh[r], out, 1, B, Tp, Tp, Hl, D, head_side,
+                                   head_side, head_side, head_side, kv_valid_len=Tp, mask=self.mask_ext,
+                                   scale=self.scale, workspace=workspace)
+        else:
+            sp.sp_masked_attention(self.qh[r], self.kh[r], self.vh[r], out, 1, B, Tp, Tp, Hl, D, head_side,
+                                   head_side, head_side, head_side, kv_valid_len=wl.T, scale=self.scale,
+                                   workspace=workspace)
+
     def gather_heads(self):
         wl = self.wl
         Tq_pad = wl.Tq if wl.cross else wl.T_pad

@@ -89,6 +89,34 @@ def test_attention_matches_oracle(dtype, D, R, B, Tq, Tk, Hl, kv, mask):
     assert err <= TOL[dtype], err
 
 
+# Launches with too few query tiles to fill the GPU split every tile's key range
+# over several workgroups and merge partial results; these shapes take that
+# path on a 256-CU MI355X (the workspace size reports its partial records).
+SPLIT_CASES = [
+    # D, R, B, Tq, Tk, Hl, kv_valid, mask kind
+    (128, 1, 1, 600, 2000, 2, 1990, None),       # 16 one-tile segments per query tile, key padding
+    (128, 2, 1, 1280, 3000, 4, 2990, None),      # 4 tiles per workgroup, segments across query tiles
+    (64, 1, 2, 700, 2500, 3, 2500, None),        # D = 64, two batches
+    (128, 1, 1, 600, 2000, 2, 2000, "blocks"),   # staircase mask: empty, full and partial segments
+    (128, 1, 2, 520, 1800, 2, 1800, "blocks_b"),  # per-batch masks
+    (64, 1, 1, 300, 2100, 3, 2100, "random"),    # a row with no visible key stays 0
+]
+
+
+@pytest.mark.parametrize("D,R,B,Tq,Tk,Hl,kv,mask", SPLIT_CASES)
+def test_attention_split_launch_matches_oracle(D, R, B, Tq, Tk, Hl, kv, mask):
+    say("attention split", D, R, B, Tq, Tk, Hl, kv, mask)
+    m = make_mask(mask, B, Tq, Tk, np.random.default_rng(Tq + Tk))
+    mbs = 0 if m is None or m.shape[0] == 1 else Tq * Tk
+    assert sp.sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, sp.SP_BF16, m is not None, mbs) > \
+        (0 if m is None else sp.sp_masked_attention_workspace_size(8 * R, B, Tq, Tk, 32 * Hl, D, sp.SP_BF16, True,
+                                                                   mbs))
+    got, want = run_case("bf16", D, R, B, Tq, Tk, Hl, kv, m, seed=Tk + D)
+    assert np.isfinite(got).all()
+    err = np.max(np.abs(got - want))
+    assert err <= TOL["bf16"], err
+
+
 def test_attention_single_visible_key_is_exact():
     """One visible key per row: p = 1 and the sum is 1, so o equals that V row
     bit for bit, also through bf16 MFMA."""
