@@ -57,6 +57,7 @@ constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pip
 constexpr bool kPrefetchV = false;   // read the V operands of a part one block before its PV MFMAs
 static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
+constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports
 constexpr int kSumChains = 1;         // independent accumulators of a part's row sum
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
@@ -191,6 +192,10 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(1024))) char v_lds1[T::TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) char k_lds2[NBUF > 2 ? T::TILE_BYTES : 16];
   __shared__ __attribute__((aligned(1024))) char v_lds2[NBUF > 2 ? T::TILE_BYTES : 16];
+  // class bytes of this query tile's row of the class map (user masks): read
+  // from LDS, so that looking up a tile's class never waits on global memory
+  // (a wait for a global load would also wait for the K/V tile in flight)
+  __shared__ uint8_t cls_lds[MASK ? kMaxClassTiles : 4];
   auto kbuf = [&](auto i) __attribute__((always_inline)) -> char* {
     constexpr int I = decltype(i)::value;
     return I == 0 ? k_lds0 : (I == 1 ? k_lds1 : k_lds2);
@@ -268,6 +273,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + (bm * a.Tq + (qvalid[qb] ? qrow[qb] : 0)) * int64_t(a.nkt);
+    for (int i = tid; i < a.nkt; i += BF16_THREADS) cls_lds[i] = cls_row[i];
+    __syncthreads();
   }
   // Key tiles of KT keys; with a user mask a tile's class combines the classes
   // of its BN-key class tiles, and empty tiles are skipped.  This segment runs
@@ -279,7 +286,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KT / BN; ++i) {
       const int c = kt * (KT / BN) + i;
-      const uint8_t v = c < a.nkt ? cls_row[c] : uint8_t(kTileEmpty);
+      const uint8_t v = c < a.nkt ? cls_lds[c] : uint8_t(kTileEmpty);
       any |= v != kTileEmpty;
       all &= v == kTileFull;
     }
@@ -353,22 +360,26 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // QK^T MFMAs of part k+1 while computing the exponentials of part k, so the
   // MFMA unit has independent work while the VALU runs the softmax; the rare
   // rescale branch comes after.
-  auto compute = [&](int kt, const char* kb_, const char* vb_) __attribute__((always_inline)) {
+  // Visibility words of this lane's rows for the BN-key class tiles of tile
+  // kt (partial tiles only).  They are loaded one tile ahead, right after that
+  // tile's K/V loads, and so have arrived by the wait for those.
+  using MaskWords = uint64_t[QB][KT / BN];
+  auto load_words = [&](int kt, MaskWords& mw) __attribute__((always_inline)) {
+    if (!MASK || kt >= nkt_eff || tile_class(kt) != kTilePartial) return;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int c = 0; c < KT / BN; ++c) {
+        const int ct = kt * (KT / BN) + c;
+        mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][ct] : 0ull;
+      }
+  };
+  auto compute = [&](int kt, const char* kb_, const char* vb_, const MaskWords& mw) __attribute__((always_inline)) {
     constexpr int NP = KT / 32;   // parts per tile
     const int64_t key0 = int64_t(kt) * KT;
     const uint8_t cls = tile_class(kt);
     const bool edge = (MASK && cls == kTilePartial) || key0 + KT > a.kv_end;
     // visibility words of this lane's rows for the BN-key class tiles of this tile
-    uint64_t mw[QB][KT / BN];
-    if (MASK && cls == kTilePartial) {
-#pragma unroll
-      for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-        for (int c = 0; c < KT / BN; ++c) {
-          const int ct = kt * (KT / BN) + c;
-          mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][ct] : 0ull;
-        }
-    }
     // S^T of part kb (keys x queries).  The K fragment (key 32*kb + l32,
     // chunk 2*ks + h) feeds every query block.  Lane (l32, h), register v then
     // holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
@@ -523,7 +534,9 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   ahead[0] = MASK ? next_tile(kt_first - 1) : kt_first;
 #pragma unroll
   for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff);
+  MaskWords mwb[NBUF] = {};   // stage S computes with mwb[S]
   if (ahead[0] < nkt_eff) issue(ahead[0], kbuf(I0{}), vbuf(I0{}));
+  load_words(ahead[0], mwb[0]);
   if constexpr (NBUF > 2) {
     if (ahead[1] < nkt_eff) issue(ahead[1], kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
   }
@@ -543,7 +556,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     ahead[NBUF - 1] = next_tile(ahead[NBUF - 2] < nkt_eff ? ahead[NBUF - 2] : nkt_eff);
     using NX = std::integral_constant<int, (S + NBUF - 1) % NBUF>;
     if (ahead[NBUF - 2] < nkt_eff) issue(ahead[NBUF - 2], kbuf(NX{}), vbuf(NX{}));
-    compute(kt, kbuf(sidx), vbuf(sidx));
+    load_words(ahead[0], mwb[(S + 1) % NBUF]);
+    compute(kt, kbuf(sidx), vbuf(sidx), mwb[S]);
     return true;
   };
   for (;;) {
@@ -979,6 +993,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (dtype == SP_BF16 && ((KT - 1) * (ks.token > vs.token ? ks.token : vs.token) + D) * eb >= (int64_t(1) << 31))
     return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
+  if (dtype == SP_BF16 && has_mask && nkt > kMaxClassTiles) return SP_ERR_UNSUPPORTED;
   const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride);
   if (has_mask && (workspace == nullptr || workspace_bytes < size_t(mask_bytes))) return SP_ERR_INVALID_ARG;
   if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
