@@ -86,7 +86,7 @@ struct AttnArgs {
   const uint8_t* mask;                   // (B, Tq, Tk) or null
   int64_t mask_bs;                       // batch stride of mask (0 = shared)
   const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt), BM x BN tiles
-  const uint64_t* bits;                  // visibility words (Bm, Tq, nkt): bit j = key BN*kt + j
+  const uint64_t* bits;                  // visibility words (Bm, nkt, Tq): bit j = key BN*kt + j
   int32_t nqt, nkt;                      // query tiles of this kernel, key tiles of BN
   int32_t nqt_cls;                       // query tiles of the class map (height BM)
   float c;                               // scale * log2(e)
@@ -272,7 +272,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + (bm * a.Tq + (qvalid[qb] ? qrow[qb] : 0)) * int64_t(a.nkt);
+    for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + bm * a.nkt * a.Tq + (qvalid[qb] ? qrow[qb] : 0);
     for (int i = tid; i < a.nkt; i += BF16_THREADS) cls_lds[i] = cls_row[i];
     __syncthreads();
   }
@@ -371,7 +371,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
       for (int c = 0; c < KT / BN; ++c) {
         const int ct = kt * (KT / BN) + c;
-        mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][ct] : 0ull;
+        mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][int64_t(ct) * a.Tq] : 0ull;
       }
   };
   auto compute = [&](int kt, const char* kb_, const char* vb_, const MaskWords& mw) __attribute__((always_inline)) {
@@ -839,7 +839,7 @@ __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* 
     } else {
       for (int c = 0; c < n; ++c) word |= uint64_t(p[c] != 0) << c;
     }
-    bits[(b * Tq + row) * int64_t(nkt) + kt] = word;
+    bits[(b * nkt + kt) * Tq + row] = word;   // rows contiguous per class tile
     any |= word != 0;
     all &= word == full;
   }

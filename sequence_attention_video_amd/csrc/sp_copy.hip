@@ -121,11 +121,19 @@ struct MaskPadArgs {
   uint8_t* out;        // (B, Tp, Tp)
   int64_t T, Tp;
   int64_t total;       // B*Tp*Tp
+  int64_t in_bytes;    // B*T*T
 };
+
+typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef uint32_t u32x4_a16 __attribute__((ext_vector_type(4)));
 
 // Each thread writes 16 consecutive output bytes (flat order).  Output byte
 // (b, i, j): i < T and j < T -> in[b, i, j]; i >= T and j < T -> 1 (a pad query
 // row sees every real key); j >= T -> 0 (pad keys are hidden from every row).
+// Inside the copied block (the common case) the 16 source bytes are
+// contiguous at any byte alignment: they come from five aligned dwords (one
+// 4-aligned dwordx4 load and one dword load) and a byte shift; chunks that
+// cross a row end, the pad rows and the buffer's last bytes go byte by byte.
 __global__ __launch_bounds__(kThreads) void pad_mask_kernel(MaskPadArgs a) {
   const int64_t p0 = (int64_t(blockIdx.x) * kThreads + threadIdx.x) * 16;
   if (p0 >= a.total) return;
@@ -134,6 +142,24 @@ __global__ __launch_bounds__(kThreads) void pad_mask_kernel(MaskPadArgs a) {
   int64_t rem = p0 - b * plane;
   int64_t i = rem / a.Tp;
   int64_t j = rem - i * a.Tp;
+  if (i < a.T && j + 16 <= a.T && p0 + 16 <= a.total) {
+    const uintptr_t addr = reinterpret_cast<uintptr_t>(a.in) + uintptr_t((b * a.T + i) * a.T + j);
+    const uintptr_t base = addr & ~uintptr_t(3);
+    // dwords past the last one holding a mask byte are never read
+    const uintptr_t lim = (reinterpret_cast<uintptr_t>(a.in) + uintptr_t(a.in_bytes) + 3) & ~uintptr_t(3);
+    if (base + 20 <= lim) {
+      const u32x4_a4 lo = *reinterpret_cast<const u32x4_a4*>(base);
+      const uint32_t hi = *reinterpret_cast<const uint32_t*>(base + 16);
+      const uint32_t sh = uint32_t(addr & 3);
+      u32x4_a16 w;
+      w.x = __builtin_amdgcn_alignbyte(lo.y, lo.x, sh);
+      w.y = __builtin_amdgcn_alignbyte(lo.z, lo.y, sh);
+      w.z = __builtin_amdgcn_alignbyte(lo.w, lo.z, sh);
+      w.w = __builtin_amdgcn_alignbyte(hi, lo.w, sh);
+      *reinterpret_cast<u32x4_a16*>(a.out + p0) = w;
+      return;
+    }
+  }
   uint8_t v[16];
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
@@ -270,6 +296,7 @@ extern "C" sp_status sp_pad(const void* x, int64_t x_batch_stride, void* y, int6
     m.T = T;
     m.Tp = T_pad;
     m.total = B * T_pad * T_pad;
+    m.in_bytes = B * T * T;
     const int64_t threads = div_up(m.total, 16);
     hipLaunchKernelGGL(pad_mask_kernel, dim3(unsigned(div_up(threads, kThreads))), dim3(kThreads), 0, s, m);
     if (launch_status() != SP_OK) return SP_ERR_HIP;
