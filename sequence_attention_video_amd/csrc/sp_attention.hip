@@ -14,11 +14,11 @@
 //     kernel is templated on query blocks per wave (QB); two blocks per wave
 //     would let every LDS operand feed two MFMAs, but at D = 128 the registers
 //     then only allow one wave per SIMD, which measured slower;
-//   * key tiles of KT = 128 are fetched with 16-byte direct global->LDS loads
-//     into a double buffer (NBUF stages in general), one barrier per tile, and
-//     the next tile's loads overlap this tile's compute; the tile is stored as padded 1 KiB
-//     key groups (see Bf16Tile) so that the MFMA operand reads are
-//     bank-conflict free and their addresses are a lane base plus immediates;
+//   * key tiles of KT = 128 are fetched with 16-byte MUBUF loads straight into
+//     LDS (double buffer, one barrier per tile; the next tile's loads overlap
+//     this tile's compute); the tile is stored as padded 1 KiB key groups (see
+//     Bf16Tile) so that the MFMA operand reads are bank-conflict free and their
+//     addresses are a lane base plus immediates;
 //   * S^T = K Q^T with v_mfma_f32_32x32x16_bf16 (Q stays in registers as the B
 //     operand).  In the 32x32 accumulator layout a lane holds 16 keys of ONE
 //     query, so the row max/sum are in-lane plus one swap with lane^32, and the
@@ -26,17 +26,22 @@
 //     O^T += V^T P^T, whose accumulator again gives each lane one query: the
 //     softmax rescale is a per-lane scalar.  The V^T operand is read from the
 //     row-major V tile with the LDS transpose read ds_read_b64_tr_b16;
-//   * each tile is processed in parts of 32 keys, which keeps the scores and
-//     probabilities of only 32 keys in registers;
+//   * each tile is processed in parts of 32 keys, software pipelined: one
+//     scheduling block holds PV of part k-1, QK^T of part k+1 and the softmax
+//     of part k;
 //   * softmax in float32 with exp2 (scale*log2 e folded into one FMA); the
-//     running max is only raised when a half's max exceeds it by more than
-//     2^8, so the O rescale runs rarely while p stays <= 256 (exact in float32,
-//     representable in bf16); row sums add the bf16-rounded p with v_dot2;
+//     running max is raised lazily: only when some lane's sum of a part's p
+//     exceeds 256 (every p of the part is below that sum), so p stays <= 256
+//     between rescales; row sums add the bf16-rounded p with v_dot2;
 //   * user masks are classified once per call into empty/full/partial tiles:
-//     empty tiles are skipped, full tiles read no mask bytes;
+//     empty tiles are skipped, full tiles read no mask bytes, partial tiles one
+//     64-bit visibility word per row and 64 keys;
 //   * workgroup ids are remapped so that the 8 XCDs each take a contiguous run
 //     of (rank, batch, head) groups: the q-tiles sharing one head's K/V run on
-//     the same XCD and share its L2.
+//     the same XCD and share its L2;
+//   * launches with too few query tiles to fill the GPU (one rank's share)
+//     split the key range over all compute units and merge partial results
+//     (attn_combine_kernel).
 
 #include "sp_internal.h"
 
