@@ -59,7 +59,7 @@ constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
-constexpr bool kPrefetchV = false;   // read the V operands of a part one block before its PV MFMAs
+constexpr bool kOperandsFirst = false; // issue all LDS operand reads of a block before its MFMAs (measured 1 % slower)
 static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
 constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports
@@ -388,18 +388,25 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     // S^T of part kb (keys x queries).  The K fragment (key 32*kb + l32,
     // chunk 2*ks + h) feeds every query block.  Lane (l32, h), register v then
     // holds key 32*kb + 8*(v/4) + 4*h + v%4 of query l32.
-    auto qk = [&](int kb, f32x16 (&sx)[QB]) __attribute__((always_inline)) {
+    auto load_k = [&](int kb, bf16x8 (&kx)[NKS]) __attribute__((always_inline)) {
+#pragma unroll
+      for (int ks = 0; ks < NKS; ++ks)
+        // offset(32*kb + l32, 2*ks + h) - offset(l32, h) is lane-independent
+        kx[ks] = *reinterpret_cast<const bf16x8*>(kb_ + k_base + (T::offset(32 * kb, 2 * ks) - T::offset(0, 0)));
+    };
+    auto qk_f = [&](const bf16x8 (&kx)[NKS], f32x16 (&sx)[QB]) __attribute__((always_inline)) {
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) sx[qb] = f32x16{};
 #pragma unroll
-      for (int ks = 0; ks < NKS; ++ks) {
-        // offset(32*kb + l32, 2*ks + h) - offset(l32, h) is lane-independent
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(
-            kb_ + k_base + (T::offset(32 * kb, 2 * ks) - T::offset(0, 0)));
+      for (int ks = 0; ks < NKS; ++ks)
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb)
-          sx[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qf[qb][ks], sx[qb], 0, 0, 0);
-      }
+          sx[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kx[ks], qf[qb][ks], sx[qb], 0, 0, 0);
+    };
+    auto qk = [&](int kb, f32x16 (&sx)[QB]) __attribute__((always_inline)) {
+      bf16x8 kx[NKS];
+      load_k(kb, kx);
+      qk_f(kx, sx);
     };
     // O^T += V^T P^T for part kb.  B element e of lane half h is key
     // 16*j2 + 8*(e/4) + 4*h + e%4 of the part.  The V^T operand takes the same
@@ -459,7 +466,6 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     };
     f32x16 s_cur[QB], s_nxt[QB];
     bf16x8 p_prev[QB][2], p_cur[QB][2];
-    bf16x8 v_prev[NDB][2], v_cur[NDB][2];   // V fragments one part ahead (kPrefetchV)
     qk(0, s_cur);
 #pragma unroll
     for (int kb = 0; kb < NP; ++kb) {
@@ -483,14 +489,19 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
       // the next part (independent MFMA chains) around the exponentials of this
       // part.  p of this part is computed against the running max and rounded
       // to bf16 (the B operands of PV).
-      if constexpr (kPrefetchV) {
-        // V fragments of part kb-1 were read in the previous block
-        if (kb > 0) pv_f(v_prev, p_prev);
-        load_v(kb, v_cur);
+      if constexpr (kOperandsFirst) {
+        // every LDS operand read of the block first (their latency then hides
+        // behind the PV MFMAs), then the MFMAs and the softmax
+        bf16x8 vx[NDB][2], kx[NKS];
+        if (kb > 0) load_v(kb - 1, vx);
+        if (kb + 1 < NP) load_k(kb + 1, kx);
+        __builtin_amdgcn_sched_barrier(0);
+        if (kb > 0) pv_f(vx, p_prev);
+        if (kb + 1 < NP) qk_f(kx, s_nxt);
       } else {
         if (kb > 0) pv(kb - 1, p_prev);
+        if (kb + 1 < NP) qk(kb + 1, s_nxt);
       }
-      if (kb + 1 < NP) qk(kb + 1, s_nxt);
       float part[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) part[qb] = exp_part(s_cur[qb], m_run[qb], p_cur[qb]);
@@ -518,15 +529,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
         for (int j2 = 0; j2 < 2; ++j2) p_prev[qb][j2] = p_cur[qb][j2];
         if (kb + 1 < NP) s_cur[qb] = s_nxt[qb];
       }
-      if constexpr (kPrefetchV) {
-#pragma unroll
-        for (int d = 0; d < NDB; ++d)
-#pragma unroll
-          for (int j2 = 0; j2 < 2; ++j2) v_prev[d][j2] = v_cur[d][j2];
-      }
     }
-    if constexpr (kPrefetchV) pv_f(v_prev, p_prev);
-    else pv(NP - 1, p_prev);
+    pv(NP - 1, p_prev);
   };
 
   // NBUF-stage pipeline over the tiles, unrolled by NBUF so that every LDS
