@@ -284,6 +284,23 @@ def main():
     ms_gh = stage(2, 3)
     ms_gather = stage(3, 4)
 
+    # -- the same step with both exchanges folded into attention's addressing
+    #    (one device only: the head-side views are strided views of the
+    #    token-side tensors); reported beside the step, not as the step
+    ref_out = step.out.clone()
+    for _ in range(max(3, args.warmup // 4)):
+        step.run_zero_copy()
+    z0 = torch.cuda.Event(enable_timing=True)
+    z1 = torch.cuda.Event(enable_timing=True)
+    z0.record(stream)
+    for _ in range(args.steps):
+        step.run_zero_copy()
+    z1.record(stream)
+    torch.cuda.synchronize()
+    ms_zero = z0.elapsed_time(z1) / args.steps
+    zero_equal = bool(torch.equal(step.outz.view(torch.uint8), ref_out.view(torch.uint8)))
+    del ref_out
+
     # -- relayout bandwidth with rotating buffer sets (> 1 GB in flight defeats the 256 MB MALL)
     set_bytes = relayout_bytes
     nsets = max(2, int(math.ceil(1.2e9 / max(set_bytes, 1))))
@@ -372,6 +389,8 @@ def main():
                          "GB/s": round(gbs(relayout_o_bytes, ms_gh), 1)},
         "gather_output_tokens": {"ms": round(ms_gather, 4), "bytes": gather_bytes,
                                  "GB/s": round(gbs(gather_bytes, ms_gather), 1)},
+        "zero_copy_step": {"ms": round(ms_zero, 4), "TFLOP/s": round(attn_flops / (ms_zero * 1e-3) / 1e12, 2),
+                           "output_bytes_equal_to_step": zero_equal},
         "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),
                                         "mfma_frac": round(share_tflops / peak_mfma, 4), "R": 1,
                                         "split": share_split,

@@ -171,3 +171,48 @@ class UlyssesStep:
         self.gather_heads()
         self.gather_output_tokens(lengths)
         return self.out
+
+    # -- the same step with both exchanges folded into attention's addressing --
+    # On one device rank r's head-side view is a strided view of the padded
+    # token-side tensor: heads r*Hl.. of every token (rank stride Hl*D, token
+    # stride H*D).  Attention reads Q/K/V and writes O through those strides,
+    # so send_recv_heads and gather_heads move no bytes; the output lands in
+    # token layout, which gather_output_tokens then trims and unpads.  Same
+    # arithmetic in the same order as run(), hence the same bytes.
+    def attention_tokens(self):
+        wl = self.wl
+        B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
+        if not hasattr(self, "oz"):
+            Tq = wl.Tq if wl.cross else Tp
+            self.oz = torch.empty(B, Tq, H, D, dtype=self.kp.dtype, device=self.kp.device)
+            self.outz = torch.empty_like(self.out)
+        tok = (Hl * D, Tp * H * D, H * D, D)                 # rank, batch, token, head
+        if wl.cross:
+            Tq = wl.Tq
+            qo = (Hl * D, Tq * H * D, H * D, D)
+            sp.sp_masked_attention(self.q, self.kp, self.vp, self.oz, wl.W, B, Tq, Tp, Hl, D, qo, tok, tok, qo,
+                                   kv_valid_len=wl.T, scale=self.scale)
+        elif self.mask is not None:
+            sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
+                                   kv_valid_len=Tp, mask=self.mask_ext, scale=self.scale, workspace=self.workspace)
+        else:
+            sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
+                                   kv_valid_len=wl.T, scale=self.scale)
+
+    def gather_output_tokens_z(self, lengths):
+        wl = self.wl
+        C = wl.H * wl.D
+        if wl.cross:
+            Tq = wl.Tq
+            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Tsq, C, Tq, counts=[self.Tsq] * wl.W,
+                               in_strides=(self.Tsq * C, Tq * C))
+        else:
+            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Ts, C, wl.T, counts=lengths,
+                               in_strides=(self.Ts * C, wl.T_pad * C))
+
+    def run_zero_copy(self):
+        self.pad()
+        _, lengths = self.partition()
+        self.attention_tokens()
+        self.gather_output_tokens_z(lengths)
+        return self.outz

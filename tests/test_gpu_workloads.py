@@ -113,3 +113,24 @@ def test_workload_stages(name):
                                 None if x["mask"] is None else T, x["mask"], rows=rows)
         err = np.max(np.abs(outf[:, rows, hh] - ref[:, rows, 0]))
         assert err <= TOL[wl.dtype], (hh, err)
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_workload_zero_copy_matches_exchange_path(name):
+    """Both exchanges folded into attention's addressing (strided views of the
+    padded token-side tensors, output written in token layout): the same
+    arithmetic in the same order as the exchange path, so the same bytes."""
+    wl = WORKLOADS[name]
+    say("zero-copy", name)
+    x = make_inputs(wl)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    mask = to_dev(x["mask"]) if x["mask"] is not None else None
+    step = UlyssesStep(wl, q, k, v, mask)
+    out = step.run().clone()
+    outz = step.run_zero_copy()
+    torch.cuda.synchronize()
+    assert torch.equal(outz.view(torch.uint8), out.view(torch.uint8))
+    # the token-layout attention output is the exchange path's gather_heads result
+    Tq = wl.Tq if wl.cross else wl.T_pad
+    ot = step.ot.view(wl.W, wl.B, Tq // wl.W, wl.H, wl.D).permute(1, 0, 2, 3, 4).reshape(wl.B, Tq, wl.H, wl.D)
+    assert torch.equal(step.oz.view(torch.uint8), ot.contiguous().view(torch.uint8))
