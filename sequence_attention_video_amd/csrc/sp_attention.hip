@@ -116,19 +116,31 @@ struct TileCoord {
   int32_t head, qt;
 };
 
-// Item i (one query tile of one (rank, batch, head)): query tile fastest,
-// then head, batch, rank.
+// Item i: one query tile of one (rank, batch, head).  Without a user mask
+// every item costs the same: query tile fastest, then head, batch, rank, and
+// workgroups are remapped so that each XCD takes a contiguous run (the query
+// tiles of a head share that XCD's L2).  With a user mask the later query
+// tiles usually see more keys (causal-like masks): items are ordered by
+// query tile, last tile first, with (rank, batch, head) fastest, and
+// dispatched in that order (longest first over the whole GPU); the hardware's
+// round-robin over the 8 XCDs still keeps each head on one XCD when the
+// number of heads is a multiple of 8.
 template <bool MASK>
-__device__ __forceinline__ TileCoord decode_item(const AttnArgs& a, uint32_t rest) {
+__device__ __forceinline__ TileCoord decode_item(const AttnArgs& a, uint32_t item) {
   TileCoord t;
-  const uint32_t qi = rest % uint32_t(a.nqt);
-  rest /= uint32_t(a.nqt);
+  uint32_t qi, rest;
+  if (MASK) {
+    const uint32_t nrbh = a.nwg / uint32_t(a.nqt);
+    qi = item / nrbh;
+    rest = item - qi * nrbh;
+  } else {
+    qi = item % uint32_t(a.nqt);
+    rest = item / uint32_t(a.nqt);
+  }
   t.head = int32_t(rest % uint32_t(a.Hl));
   rest /= uint32_t(a.Hl);
   t.b = int64_t(rest % uint64_t(a.B));
   t.r = int64_t(rest / uint64_t(a.B));
-  // with a user mask, later query tiles usually see more keys (causal-like
-  // masks): start those first
   t.qt = MASK ? a.nqt - 1 - int32_t(qi) : int32_t(qi);
   return t;
 }
@@ -235,7 +247,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     u_next += kt_stop - kt_first;
     if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
   } else {
-    item = xcd_remap(blockIdx.x, a.nwg);
+    item = MASK ? blockIdx.x : xcd_remap(blockIdx.x, a.nwg);
   }
   const TileCoord tc = decode_item<MASK>(a, item);
 
@@ -679,7 +691,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   __shared__ float k_lds[BN * KST];
   __shared__ float v_lds[BN * VST];
 
-  const TileCoord tc = decode_item<MASK>(a, xcd_remap(blockIdx.x, a.nwg));
+  const TileCoord tc = decode_item<MASK>(a, MASK ? blockIdx.x : xcd_remap(blockIdx.x, a.nwg));
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
 
