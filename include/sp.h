@@ -155,7 +155,9 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * {16, 64, 128} (float32 MFMA throughout).
  * Errors: sizes < 0, null tensors, kv_valid_len < 0, a mask without a large
  * enough workspace -> SP_ERR_INVALID_ARG; other D, or (bf16) a K or V token
- * stride above 8 million elements (its 32-bit tile offsets) -> SP_ERR_UNSUPPORTED.
+ * stride above 8 million elements (its 32-bit tile offsets), or (bf16) a user
+ * mask with Tk above 4096 * 64 keys (the per-row tile classes it keeps in
+ * LDS) -> SP_ERR_UNSUPPORTED.
  */
 size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
                                           sp_dtype dtype, int32_t has_mask, int64_t mask_batch_stride);

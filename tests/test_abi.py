@@ -99,6 +99,17 @@ def test_validation_returns_before_launch(lib):
                                    None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 128, b.SP_BF16, 64,
                                    None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
+    # bf16 K/V token strides beyond the kernel's 32-bit tile offsets; a user
+    # mask over more key tiles than the kernel keeps in LDS (4096 x 64 keys).
+    # Fake, far-apart 16-byte aligned addresses: validation fails before any launch.
+    qa, ka, va, oa = (ctypes.c_void_p(x << 40) for x in (1, 2, 3, 4))
+    st = A(0, 0, 512, 128)
+    big = A(0, 0, 9_000_000, 128)
+    assert lib.sp_masked_attention(qa, st, ka, big, va, st, oa, st, 1, 1, 64, 64, 4, 128, b.SP_BF16, 64,
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+    tk = 4096 * 64 + 1
+    assert lib.sp_masked_attention(qa, st, ka, st, va, st, oa, st, 1, 1, 64, tk, 4, 128, b.SP_BF16, tk,
+                                   ctypes.c_void_p(5 << 40), 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
     # empty problems are a no-op success
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 0, 64, 1, 128, b.SP_BF16, 64,
                                    None, 0, 0.1, None, 0, None) == b.SP_OK
