@@ -49,6 +49,7 @@ __all__ = [
     "gather_output_tokens",
     "ulysses_self_attention",
     "ulysses_cross_attention",
+    "joint_av_block",
     "reference_attention",
 ]
 
@@ -341,7 +342,7 @@ def ulysses_self_attention(q, k, v, world_size: int, scale: float,
 
 def ulysses_cross_attention(q, k, v, world_size: int, scale: float,
                             kv_valid_len: int, t_kv_pad: int,
-                            keep_intermediates: bool = False):
+                            keep_intermediates: bool = False, t_q_pad: int | None = None):
     """Cross-attention variant: only K/V go through the exchange.
 
     [SP] 换头: for the video->audio cross-attention the query side is sliced on
@@ -350,23 +351,60 @@ def ulysses_cross_attention(q, k, v, world_size: int, scale: float,
     place; k, v (B, Tkv, H, D) hold ``kv_valid_len`` real keys, padded to
     ``t_kv_pad`` (R12) and exchanged; the output goes back through
     gather_heads and gather_output_tokens to (B, Tq, H, D).
+
+    ``t_q_pad``: the query modality's own padded length ([SP] 补齐 pads each
+    modality's sequence to a multiple of world_size; 还原 unpads the output to
+    the caller's length).  Needed when Tq is not a multiple of world_size (an
+    audio query sequence); pad query rows attend like any row and are dropped
+    by the unpad.  Default: Tq itself.
     """
     b, tq, h, d = q.shape
     if h % world_size != 0:
         raise ValueError(f"H={h} is not divisible by world_size={world_size}")
     hl = h // world_size
+    tq_pad = tq if t_q_pad is None else t_q_pad
+    q = pad_tokens(q, tq_pad)
     kp, vp = pad_tokens(k[:, :kv_valid_len], t_kv_pad), pad_tokens(v[:, :kv_valid_len], t_kv_pad)
     compute_sequence_partition(t_kv_pad, world_size)
     kh, vh = (send_recv_heads(token_shards(a, world_size)) for a in (kp, vp))
     oh = np.stack([attention_heads(q[:, :, r * hl:(r + 1) * hl], kh[r], vh[r], scale,
                                    kv_valid_len, None)
-                   for r in range(world_size)])             # (W, B, Tq, Hl, D)
-    ot = gather_heads(oh)                                   # (W, B, Tq/W, H, D)
-    offsets, lengths = compute_sequence_partition(tq, world_size)
+                   for r in range(world_size)])             # (W, B, Tq_pad, Hl, D)
+    ot = gather_heads(oh)                                   # (W, B, Tq_pad/W, H, D)
+    offsets, lengths = compute_sequence_partition(tq_pad, world_size)
     local = [ot[r].reshape(b, lengths[r], h * d) for r in range(world_size)]
     out = gather_output_tokens(local, lengths, tq).reshape(b, tq, h, d)
     if keep_intermediates:
         return out, dict(k_heads=kh, v_heads=vh, o_heads=oh, o_tokens=ot)
+    return out
+
+
+def joint_av_block(parts: dict, world_size: int, video_tokens: int, audio_tokens: int):
+    """The joint audio-video attention of one block on the sequence-parallel
+    path, the pages' per-step chain around it ([SP] "token 切片、换头、gather
+    还原": 补齐 per modality, 换头 for self-attention, and for the cross
+    attentions only K/V exchanged while the rank slices the query side).
+
+    Each modality is padded to its own multiple of world_size
+    (pad_modality_for_uniform_sharding).  ``parts`` maps "video_self",
+    "audio_self", "v2a" (video queries, audio keys) and "a2v" (audio queries,
+    video keys) to dicts of float64 q, k, v (B, T, H, D) with the modality
+    lengths of their roles; every part uses scale 1/sqrt(D).  Returns the four
+    outputs, each (B, Tq, H, D) with the real query tokens.
+    """
+    tv_pad = padded_length(video_tokens, world_size)
+    ta_pad = padded_length(audio_tokens, world_size)
+    out = {}
+    for name in ("video_self", "audio_self"):
+        x = parts[name]
+        d = x["q"].shape[-1]
+        out[name] = ulysses_self_attention(x["q"], x["k"], x["v"], world_size, 1.0 / np.sqrt(d))
+    for name, t_kv, t_kv_pad, t_q_pad in (("v2a", audio_tokens, ta_pad, tv_pad),
+                                           ("a2v", video_tokens, tv_pad, ta_pad)):
+        x = parts[name]
+        d = x["q"].shape[-1]
+        out[name] = ulysses_cross_attention(x["q"], x["k"], x["v"], world_size, 1.0 / np.sqrt(d),
+                                            t_kv, t_kv_pad, t_q_pad=t_q_pad)
     return out
 
 

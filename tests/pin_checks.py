@@ -284,3 +284,41 @@ def check_sharded_equals_unsharded_cross(O):
         sharded = O.ulysses_cross_attention(q, k, v, w, 0.45, tkv, tkv_pad)
         ref = O.reference_attention(q, k, v, 0.45)
         assert np.max(np.abs(sharded - ref)) < 1e-12
+
+
+def check_cross_query_padding(O):
+    """A query sequence that is not a multiple of W is padded to its own
+    multiple ([SP] 补齐, per modality) and unpadded at the end (还原): the
+    sharded result equals unsharded attention on the real queries; without
+    the padding the partition raises (切分)."""
+    rng = np.random.default_rng(16)
+    for (b, tq, tkv, tkv_pad, h, d, w) in [(1, 13, 9, 12, 8, 4, 4), (2, 7, 6, 6, 6, 3, 3)]:
+        q = rng.standard_normal((b, tq, h, d))
+        k, v = rng.standard_normal((b, tkv, h, d)), rng.standard_normal((b, tkv, h, d))
+        tq_pad = O.padded_length(tq, w)
+        sharded = O.ulysses_cross_attention(q, k, v, w, 0.45, tkv, tkv_pad, t_q_pad=tq_pad)
+        assert sharded.shape == q.shape
+        assert np.max(np.abs(sharded - O.reference_attention(q, k, v, 0.45))) < 1e-12
+        try:
+            O.ulysses_cross_attention(q, k, v, w, 0.45, tkv, tkv_pad)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError("an unpadded query length that W does not divide must raise")
+
+
+def check_joint_av_block(O):
+    """The joint audio-video block: each modality padded to its own multiple
+    of W; all four attentions equal unsharded attention on the real tokens."""
+    rng = np.random.default_rng(17)
+    w, b, h, tv, ta = 4, 1, 8, 22, 7
+    shapes = {"video_self": (tv, tv, 8), "audio_self": (ta, ta, 4), "v2a": (tv, ta, 4), "a2v": (ta, tv, 4)}
+    parts = {}
+    for name, (tq, tk, d) in shapes.items():
+        parts[name] = dict(q=rng.standard_normal((b, tq, h, d)), k=rng.standard_normal((b, tk, h, d)),
+                           v=rng.standard_normal((b, tk, h, d)))
+    out = O.joint_av_block(parts, w, tv, ta)
+    for name, x in parts.items():
+        ref = O.reference_attention(x["q"], x["k"], x["v"], 1.0 / np.sqrt(x["q"].shape[-1]))
+        assert out[name].shape == x["q"].shape, name
+        assert np.max(np.abs(out[name] - ref)) < 1e-12, name

@@ -18,7 +18,8 @@ CHECKS = [
     P.check_relayout_shapes, P.check_attention_golden, P.check_attention_brute_force,
     P.check_attention_closed_forms, P.check_garbage_pad_invariance, P.check_gather_output,
     P.check_sharded_equals_unsharded_self, P.check_sharded_equals_unsharded_mask,
-    P.check_sharded_equals_unsharded_cross, P.check_attention_sdpa,
+    P.check_sharded_equals_unsharded_cross, P.check_attention_sdpa, P.check_cross_query_padding,
+    P.check_joint_av_block,
 ]
 
 MUTANTS = {
@@ -43,6 +44,9 @@ MUTANTS = {
     "cross: all ranks use the first heads": ("attention_heads(q[:, :, r * hl:(r + 1) * hl], kh[r]",
                                              "attention_heads(q[:, :, 0:hl], kh[r]"),
     "user mask rows/cols transposed": ("out[:, :t, :t] = (m != 0)", "out[:, :t, :t] = (m != 0).transpose(0, 2, 1)"),
+    "cross: query padding ignored": ("q = pad_tokens(q, tq_pad)", "q = q"),
+    "joint: cross keys from the wrong modality": ('(("v2a", audio_tokens, ta_pad, tv_pad),',
+                                                 '(("v2a", video_tokens, tv_pad, tv_pad),'),
 }
 
 

@@ -145,3 +145,11 @@ def test_bf16_widening():
     want = [1.0, -2.5, 0.0, -0.0, (2 - 2 ** -7) * 2.0 ** 127, 2.0 ** -133]
     assert got.tolist() == want
     assert math.copysign(1.0, got[3]) < 0
+
+
+def test_cross_query_padding():
+    P.check_cross_query_padding(O)
+
+
+def test_joint_av_block():
+    P.check_joint_av_block(O)
