@@ -211,6 +211,9 @@ def main():
     from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
 
     binding.load()          # fails loudly if the HIP library is missing
+    if args.config == "joint_av":
+        bench_joint(args)
+        return
     wl = WORKLOADS[args.config]
     dev = torch.device("cuda:0")
     log("inputs", wl.name)
@@ -426,6 +429,92 @@ def main():
         "wall_s_timed": round(wall, 3),
         "checks": {"output_finite": finite, "relayout_round_trip_bytes_equal": round_trip},
         "kernel_source_hash": src_hash,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def bench_joint(args):
+    """The joint audio-video block: four attentions (video self, audio self,
+    video->audio, audio->video), each through its whole path; a step runs all
+    four.  value = attention flops of the four / step time."""
+    import numpy as np
+    import torch
+
+    from sequence_attention_video_amd.pipeline import JointAVStep
+    from sequence_attention_video_amd.workloads import JOINT_AV, make_joint_inputs
+
+    jw = JOINT_AV
+    log("inputs", jw.name)
+    x = make_joint_inputs(jw)
+    step = JointAVStep(jw, x)
+    parts = jw.parts()
+    flops = {n: 4 * wl.D * wl.H * wl.B * wl.q_tokens_pad * wl.T for n, wl in parts.items()}
+    total = sum(flops.values())
+    step.run()
+    torch.cuda.synchronize()
+    log("warmup", args.warmup)
+    for _ in range(args.warmup):
+        step.run()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    names = JointAVStep.PARTS
+    n = len(names)
+    # per step: n + 1 part boundaries, then the video self-attention launch's two
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(n + 3)] for _ in range(args.steps)]
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record(stream)
+    for i in range(args.steps):
+        e = ev[i]
+        for j, name in enumerate(names):
+            e[j].record(stream)
+            s_ = step.steps[name]
+            s_.pad()
+            _, lengths = s_.partition()
+            s_.send_recv_heads()
+            if name == "video_self":            # the dominant kernel, timed on its own
+                e[n + 1].record(stream)
+            s_.attention()
+            if name == "video_self":
+                e[n + 2].record(stream)
+            s_.gather_heads()
+            s_.gather_output_tokens(lengths)
+        e[n].record(stream)
+    t1.record(stream)
+    torch.cuda.synchronize()
+    ms_step = t0.elapsed_time(t1) / args.steps
+    part_ms = {name: float(np.mean([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(args.steps)]))
+               for j, name in enumerate(names)}
+    ms_attn_v = float(np.mean([ev[i][n + 1].elapsed_time(ev[i][n + 2]) for i in range(args.steps)]))
+    v_tflops = flops["video_self"] / (ms_attn_v * 1e-3) / 1e12
+    finite = all(bool(torch.isfinite(o.float()).all().item()) for o in step.run().values())
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(parts["video_self"], x["video_self"], args.cpu_seconds)
+    out = {
+        "metric": METRIC,
+        "value": round(total / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": jw.dtype,
+        "data": "synthetic",
+        "config": {"workload": jw.name, "B": jw.B, "W": jw.W, "H": jw.H, "Tv": jw.Tv, "Ta": jw.Ta,
+                   "Dv": jw.Dv, "Da": jw.Da},
+        "roofline": {"bound": "mfma", "achieved": round(v_tflops, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(v_tflops / PEAK_BF16_TFLOPS, 4), "traffic": None,
+                     "kernel": "attn_bf16_kernel<128> (video self-attention)",
+                     "flops_per_launch": flops["video_self"], "avg_launch_ms": round(ms_attn_v, 4)},
+        "cpu_baseline": cpu,
+        "parts": {n: {"ms": round(part_ms[n], 4), "attention_flops": flops[n],
+                      "TFLOP/s_over_path": round(flops[n] / (part_ms[n] * 1e-3) / 1e12, 2)} for n in names},
+        "checks": {"output_finite": finite},
+        "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
     }
     print(json.dumps(out), flush=True)
 

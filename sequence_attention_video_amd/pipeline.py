@@ -49,12 +49,17 @@ class UlyssesStep:
         e = lambda *s, d=dt: torch.empty(*s, dtype=d, device=device)
         self.q, self.k, self.v, self.mask = q, k, v, mask
         self.need_pad = Tp != T
+        self.need_q_pad = False
         if wl.cross:
             self.kp, self.vp = (e(B, Tp, H, D), e(B, Tp, H, D)) if self.need_pad else (k, v)
             self.kh, self.vh = e(W, B, Tp, Hl, D), e(W, B, Tp, Hl, D)
-            Tq = wl.Tq
-            self.Tsq = Tq // W
-            self.oh = e(W, B, Tq, Hl, D)
+            # the query modality is padded on its own to a multiple of W (it is
+            # sliced on the rank, never exchanged); output unpadded to Tq
+            Tq, Tqp = wl.Tq, wl.q_tokens_pad
+            self.need_q_pad = Tqp != Tq
+            self.qc = e(B, Tqp, H, D) if self.need_q_pad else q
+            self.Tsq = Tqp // W
+            self.oh = e(W, B, Tqp, Hl, D)
             self.ot = e(W, B, self.Tsq, H, D)
             self.out = e(B, Tq, H, D)
         else:
@@ -81,6 +86,9 @@ class UlyssesStep:
     # -- the step's stages, each one library call (or one host call) ----------
     def pad(self):
         wl = self.wl
+        C = wl.H * wl.D
+        if self.need_q_pad:
+            sp.sp_pad(self.q.view(wl.B, wl.Tq, C), self.qc.view(wl.B, wl.q_tokens_pad, C), wl.q_tokens_pad)
         if not self.need_pad:
             return
         if wl.cross:
@@ -88,7 +96,6 @@ class UlyssesStep:
         else:
             pairs = [(self.q, self.qp), (self.k, self.kp), (self.v, self.vp)]
         for i, (x, y) in enumerate(pairs):
-            C = wl.H * wl.D
             first = i == 0 and self.mask is not None
             sp.sp_pad(x.view(wl.B, wl.T, C), y.view(wl.B, wl.T_pad, C), wl.T_pad,
                       mask_in=self.mask if first else None, mask_out=self.mask_ext if first else None)
@@ -110,10 +117,10 @@ class UlyssesStep:
         B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
         head_side = (B * Tp * Hl * D, Tp * Hl * D, Hl * D, D)
         if wl.cross:
-            Tq = wl.Tq
+            Tq = wl.q_tokens_pad
             qs = (Hl * D, Tq * H * D, H * D, D)            # rank r's heads of the unexchanged Q
             os_ = (B * Tq * Hl * D, Tq * Hl * D, Hl * D, D)
-            sp.sp_masked_attention(self.q, self.kh, self.vh, self.oh, wl.W, B, Tq, Tp, Hl, D,
+            sp.sp_masked_attention(self.qc, self.kh, self.vh, self.oh, wl.W, B, Tq, Tp, Hl, D,
                                    qs, head_side, head_side, os_, kv_valid_len=wl.T, scale=self.scale)
             return
         if self.mask is not None:
@@ -135,10 +142,10 @@ class UlyssesStep:
         B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
         head_side = (B * Tp * Hl * D, Tp * Hl * D, Hl * D, D)
         if wl.cross:
-            Tq = wl.Tq
+            Tq = wl.q_tokens_pad
             qs = (Hl * D, Tq * H * D, H * D, D)
             os_ = (B * Tq * Hl * D, Tq * Hl * D, Hl * D, D)
-            q = self.q[:, :, r * Hl:(r + 1) * Hl]
+            q = self.qc[:, :, r * Hl:(r + 1) * Hl]
             sp.sp_masked_attention(q, self.kh[r], self.vh[r], out, 1, B, Tq, Tp, Hl, D, qs, head_side, head_side,
                                    os_, kv_valid_len=wl.T, scale=self.scale, workspace=workspace)
         elif self.mask is not None:
@@ -152,7 +159,7 @@ class UlyssesStep:
 
     def gather_heads(self):
         wl = self.wl
-        Tq_pad = wl.Tq if wl.cross else wl.T_pad
+        Tq_pad = wl.q_tokens_pad if wl.cross else wl.T_pad
         sp.sp_relayout_heads([self.oh], [self.ot], wl.W, wl.B, Tq_pad, wl.H, wl.D, sp.SP_HEADS_TO_TOKENS)
 
     def gather_output_tokens(self, lengths):
@@ -183,14 +190,14 @@ class UlyssesStep:
         wl = self.wl
         B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
         if not hasattr(self, "oz"):
-            Tq = wl.Tq if wl.cross else Tp
+            Tq = wl.q_tokens_pad if wl.cross else Tp
             self.oz = torch.empty(B, Tq, H, D, dtype=self.kp.dtype, device=self.kp.device)
             self.outz = torch.empty_like(self.out)
         tok = (Hl * D, Tp * H * D, H * D, D)                 # rank, batch, token, head
         if wl.cross:
-            Tq = wl.Tq
+            Tq = wl.q_tokens_pad
             qo = (Hl * D, Tq * H * D, H * D, D)
-            sp.sp_masked_attention(self.q, self.kp, self.vp, self.oz, wl.W, B, Tq, Tp, Hl, D, qo, tok, tok, qo,
+            sp.sp_masked_attention(self.qc, self.kp, self.vp, self.oz, wl.W, B, Tq, Tp, Hl, D, qo, tok, tok, qo,
                                    kv_valid_len=wl.T, scale=self.scale)
         elif self.mask is not None:
             sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
@@ -203,9 +210,9 @@ class UlyssesStep:
         wl = self.wl
         C = wl.H * wl.D
         if wl.cross:
-            Tq = wl.Tq
-            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Tsq, C, Tq, counts=[self.Tsq] * wl.W,
-                               in_strides=(self.Tsq * C, Tq * C))
+            Tqp = wl.q_tokens_pad
+            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Tsq, C, wl.Tq, counts=[self.Tsq] * wl.W,
+                               in_strides=(self.Tsq * C, Tqp * C))
         else:
             sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Ts, C, wl.T, counts=lengths,
                                in_strides=(self.Ts * C, wl.T_pad * C))
@@ -216,3 +223,26 @@ class UlyssesStep:
         self.attention_tokens()
         self.gather_output_tokens_z(lengths)
         return self.outz
+
+
+class JointAVStep:
+    """The joint audio-video attention of one block: video self-attention,
+    audio self-attention, video->audio and audio->video cross-attention, each
+    on the sequence-parallel path over the same W virtual ranks (page "LTX-2
+    序列并行拆解", section "token 切片、换头、gather 还原": 补齐 per modality;
+    for cross-attention the rank slices the query side and only K/V go
+    through the exchange).  Each part is one UlyssesStep; the modalities are
+    padded independently (video 6144 -> 6144, audio 987 -> 992 at W = 8)."""
+
+    PARTS = ("video_self", "audio_self", "v2a", "a2v")
+
+    def __init__(self, jw, inputs: dict, device="cuda"):
+        self.jw = jw
+        self.steps = {}
+        for name, wl in jw.parts().items():
+            x = inputs[name]
+            q, k, v = (to_device(x[n], wl.dtype, device) for n in "qkv")
+            self.steps[name] = UlyssesStep(wl, q, k, v, None, device=device)
+
+    def run(self) -> dict:
+        return {name: self.steps[name].run() for name in self.PARTS}

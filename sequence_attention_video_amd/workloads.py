@@ -69,7 +69,9 @@ class Workload:
 
     @property
     def q_tokens_pad(self) -> int:
-        return self.Tq if self.cross else self.T_pad
+        """Query rows the path computes: the query modality padded to a
+        multiple of W (cross-attention queries are padded on their own)."""
+        return self.W * (-(-self.Tq // self.W)) if self.cross else self.T_pad
 
 
 WORKLOADS = {
@@ -85,6 +87,45 @@ WORKLOADS = {
 }
 
 ORDER = ["tiny", "video_self", "uneven_mask", "cross_v2a", "long_hires"]
+
+
+@dataclass(frozen=True)
+class JointWorkload:
+    """One joint audio-video attention block: video self-attention, audio
+    self-attention, video->audio and audio->video cross-attention, each
+    modality padded to its own multiple of W.  Video: 16 latent frames of
+    16 x 24 tokens (as video_self); audio: 987 tokens (as cross_v2a's keys),
+    padded to 992.  Video self-attention uses D = 128, the audio and cross
+    attentions D = 64 (the audio stream's width); activations N(0, 1/D)."""
+    index: int = 6
+    name: str = "joint_av"
+    B: int = 1
+    W: int = 8
+    H: int = 32
+    Tv: int = 6144
+    Ta: int = 987
+    Dv: int = 128
+    Da: int = 64
+    dtype: str = "bf16"
+
+    def parts(self) -> dict:
+        common = dict(B=self.B, W=self.W, H=self.H, dtype=self.dtype, std="1/sqrt(D)", mask="key")
+        return {
+            "video_self": Workload(self.index, "joint_video_self", T=self.Tv, D=self.Dv, **common),
+            "audio_self": Workload(self.index, "joint_audio_self", T=self.Ta, D=self.Da, **common),
+            "v2a": Workload(self.index, "joint_v2a", T=self.Ta, D=self.Da, cross=True, Tq=self.Tv, **common),
+            "a2v": Workload(self.index, "joint_a2v", T=self.Tv, D=self.Da, cross=True, Tq=self.Ta, **common),
+        }
+
+
+JOINT_AV = JointWorkload()
+JOINT_SEED_OFFSET = {"video_self": 0, "audio_self": 10, "v2a": 20, "a2v": 30}
+
+
+def make_joint_inputs(jw: JointWorkload) -> dict:
+    """Per part (see JointWorkload.parts) the make_inputs dict, seeds
+    1000 * index + part offset + {q: 0, k: 1, v: 2}."""
+    return {name: make_inputs(wl, JOINT_SEED_OFFSET[name]) for name, wl in jw.parts().items()}
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:

@@ -1,0 +1,71 @@
+"""The joint audio-video block (video self-attention, audio self-attention,
+video->audio and audio->video cross-attention, each modality padded to its own
+multiple of W) at full size on the GPU, against the CPU oracle:
+
+* the audio query modality's padding (987 -> 992 rows) bit-exact;
+* every part's final output on sampled query rows (first, last, shard
+  boundaries, the last real row) within 2e-2 of unsharded float64 attention
+  on the real tokens (the sharded == unsharded invariant);
+* the zero-copy form of every part byte-identical to its exchange path.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from sequence_attention_video_amd.pipeline import JointAVStep
+from sequence_attention_video_amd.workloads import JOINT_AV, make_joint_inputs
+from tests.gpu_util import f64, raw, say
+
+pytestmark = pytest.mark.gpu
+
+TOL = 2e-2
+
+
+def sample_rows(n, shard, rng):
+    rows = {0, 1, n - 1, n - 2}
+    for s in range(1, max(1, n // shard)):
+        rows.update({s * shard - 1, s * shard})
+    rows.update(int(x) for x in rng.integers(0, n, 6))
+    return np.array(sorted(r for r in rows if 0 <= r < n))
+
+
+def test_joint_av_block():
+    say("joint_av")
+    jw = JOINT_AV
+    x = make_joint_inputs(jw)
+    step = JointAVStep(jw, x)
+    outs = step.run()
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    parts = jw.parts()
+    # the audio queries of the audio->video cross-attention, padded on their own
+    a2v = step.steps["a2v"]
+    assert a2v.need_q_pad
+    assert raw(a2v.qc).tobytes() == O.pad_tokens(x["a2v"]["q"], parts["a2v"].q_tokens_pad).tobytes()
+    for name, wl in parts.items():
+        say("joint_av check", name)
+        got = f64(raw(outs[name]))
+        tq = wl.q_tokens
+        assert got.shape == (wl.B, tq, wl.H, wl.D)
+        assert np.isfinite(got).all()
+        rows = sample_rows(tq, wl.q_tokens_pad // wl.W, rng)
+        q = f64(x[name]["q"])[:, rows]
+        want = O.attention_heads(q, f64(x[name]["k"]), f64(x[name]["v"]), 1.0 / math.sqrt(wl.D), wl.T, None)
+        err = np.max(np.abs(got[:, rows] - want))
+        assert err <= TOL, (name, err)
+
+
+def test_joint_av_zero_copy_matches_exchange_path():
+    say("joint_av zero-copy")
+    jw = JOINT_AV
+    step = JointAVStep(jw, make_joint_inputs(jw))
+    for name in JointAVStep.PARTS:
+        s = step.steps[name]
+        out = s.run().clone()
+        outz = s.run_zero_copy()
+        torch.cuda.synchronize()
+        assert torch.equal(outz.view(torch.uint8), out.view(torch.uint8)), name
