@@ -59,11 +59,9 @@ constexpr int BM32 = 128;            // query rows per fp32 workgroup
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
-constexpr bool kOperandsFirst = false; // issue all LDS operand reads of a block before its MFMAs (measured 1 % slower)
 static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
 constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports
-constexpr int kSumChains = 1;         // independent accumulators of a part's row sum
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
@@ -458,8 +456,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     // operands; returns this lane's sum of the rounded p (v_dot2 with ones)
     auto exp_part = [&](const f32x16& sx, float m, bf16x8 (&px)[2]) __attribute__((always_inline)) -> float {
       const float nm = -m;
-      // kSumChains independent dot2 accumulators, so the sum is not one serial chain
-      float sums[kSumChains] = {};
+      float sum = 0.f;
 #pragma unroll
       for (int j2 = 0; j2 < 2; ++j2) {
 #pragma unroll
@@ -468,13 +465,10 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int e = 0; e < 8; e += 2) {
           const bf16x2 pair = {px[j2][e], px[j2][e + 1]};
-          float& acc = sums[(4 * j2 + e / 2) % kSumChains];
-          acc = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, acc, false);
+          sum = __builtin_amdgcn_fdot2_f32_bf16(pair, bf16x2{(__bf16)1.0f, (__bf16)1.0f}, sum, false);
         }
       }
-#pragma unroll
-      for (int c = 1; c < kSumChains; ++c) sums[0] += sums[c];
-      return sums[0];
+      return sum;
     };
     f32x16 s_cur[QB], s_nxt[QB];
     bf16x8 p_prev[QB][2], p_cur[QB][2];
@@ -501,19 +495,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
       // the next part (independent MFMA chains) around the exponentials of this
       // part.  p of this part is computed against the running max and rounded
       // to bf16 (the B operands of PV).
-      if constexpr (kOperandsFirst) {
-        // every LDS operand read of the block first (their latency then hides
-        // behind the PV MFMAs), then the MFMAs and the softmax
-        bf16x8 vx[NDB][2], kx[NKS];
-        if (kb > 0) load_v(kb - 1, vx);
-        if (kb + 1 < NP) load_k(kb + 1, kx);
-        __builtin_amdgcn_sched_barrier(0);
-        if (kb > 0) pv_f(vx, p_prev);
-        if (kb + 1 < NP) qk_f(kx, s_nxt);
-      } else {
-        if (kb > 0) pv(kb - 1, p_prev);
-        if (kb + 1 < NP) qk(kb + 1, s_nxt);
-      }
+      if (kb > 0) pv(kb - 1, p_prev);
+      if (kb + 1 < NP) qk(kb + 1, s_nxt);
       float part[QB];
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb) part[qb] = exp_part(s_cur[qb], m_run[qb], p_cur[qb]);
