@@ -19,6 +19,9 @@ Pages cited (title, then the section on that page):
         "全局注意力没有变，只是分布方式变了" (the invariants).
 * [MG]  "Multi-GPU Inference" (LTX-2 ``docs/multigpu/README.md``), table
         "Capabilities", row "Sequence parallelism (SP)".
+* [LC]  "LongCat-Video上下文并行技术如何实现高效的多GPU推理", section
+        "智能张量拆分策略" (the 2-D height x width split and its near-square
+        choice of split ratio).
 
 Readings of points the pages leave open are numbered R1..R13 and listed in the
 repository's design notes; each function names the ones it relies on.
@@ -50,6 +53,10 @@ __all__ = [
     "ulysses_self_attention",
     "ulysses_cross_attention",
     "joint_av_block",
+    "get_optimal_split",
+    "split_cp_2d",
+    "gather_cp_2d",
+    "ulysses_self_attention_2d",
     "reference_attention",
 ]
 
@@ -406,6 +413,85 @@ def joint_av_block(parts: dict, world_size: int, video_tokens: int, audio_tokens
         out[name] = ulysses_cross_attention(x["q"], x["k"], x["v"], world_size, 1.0 / np.sqrt(d),
                                             t_kv, t_kv_pad, t_q_pad=t_q_pad)
     return out
+
+
+# ---------------------------------------------------------------------------
+# the 2-D (height x width) split of the token grid
+# ---------------------------------------------------------------------------
+
+def get_optimal_split(n_ranks: int, height: int, width: int):
+    """Rank grid (split_h, split_w) for ``n_ranks`` over a height x width
+    token grid: [LC] "智能张量拆分策略" picks the split closest to a square.
+
+    R17: among factor pairs split_h * split_w = n_ranks that divide the grid
+    evenly (height % split_h == 0, width % split_w == 0), the pair closest to
+    square (smallest |split_h - split_w|); between its two orientations the
+    one whose tiles are closer to square (smallest |height/split_h -
+    width/split_w|), then the smaller split_h.  No even split -> ValueError.
+    """
+    if n_ranks < 1:
+        raise ValueError("n_ranks must be >= 1")
+    best = None
+    for a in range(1, n_ranks + 1):
+        if n_ranks % a:
+            continue
+        b = n_ranks // a
+        if height % a or width % b:
+            continue
+        key = (abs(a - b), abs(height // a - width // b), a)
+        if best is None or key < best[0]:
+            best = (key, (a, b))
+    if best is None:
+        raise ValueError(f"no even {n_ranks}-way split of a {height} x {width} grid")
+    return best[1]
+
+
+def split_cp_2d(x: np.ndarray, frames: int, height: int, width: int, split_h: int, split_w: int) -> np.ndarray:
+    """Every rank's tile of the token grid ([LC] split_tensor_in_cp_2d).
+
+    x: (B, T, ...) with T = frames*height*width tokens in raster order
+    (token f*height*width + y*width + x_).  Rank r = i*split_w + j holds rows
+    i*th..(i+1)*th-1 and columns j*tw..(j+1)*tw-1 of every frame (th =
+    height/split_h, tw = width/split_w), its tokens in raster order within
+    the tile.  Returns (split_h*split_w, B, frames*th*tw, ...).
+    """
+    b = x.shape[0]
+    th, tw = height // split_h, width // split_w
+    grid = x.reshape((b, frames, height, width) + x.shape[2:])
+    out = []
+    for i in range(split_h):
+        for j in range(split_w):
+            tile = grid[:, :, i * th:(i + 1) * th, j * tw:(j + 1) * tw]
+            out.append(tile.reshape((b, frames * th * tw) + x.shape[2:]))
+    return np.stack(out)
+
+
+def gather_cp_2d(tiles: np.ndarray, frames: int, height: int, width: int, split_h: int, split_w: int) -> np.ndarray:
+    """Inverse of ``split_cp_2d`` ([LC] gather_cp_2d): put every rank's tile
+    back at its rows and columns; (N, B, frames*th*tw, ...) -> (B, T, ...)."""
+    n, b = tiles.shape[:2]
+    th, tw = height // split_h, width // split_w
+    rest = tiles.shape[3:]
+    grid = np.empty((b, frames, height, width) + rest, dtype=tiles.dtype)
+    for i in range(split_h):
+        for j in range(split_w):
+            r = i * split_w + j
+            grid[:, :, i * th:(i + 1) * th, j * tw:(j + 1) * tw] = tiles[r].reshape((b, frames, th, tw) + rest)
+    return grid.reshape((b, frames * height * width) + rest)
+
+
+def ulysses_self_attention_2d(q, k, v, frames: int, height: int, width: int, n_ranks: int, scale: float):
+    """Self-attention with the 2-D split in place of the 1-D token split:
+    split_cp_2d -> send_recv_heads (each rank gathers every token of its local
+    heads, in rank-then-tile order) -> attention on the local heads ->
+    gather_heads -> gather_cp_2d.  Attention needs no token order (no mask
+    but the key-only one, and the grid needs no padding), so the result is
+    unsharded attention; q, k, v: (B, T, H, D) float64."""
+    split_h, split_w = get_optimal_split(n_ranks, height, width)
+    qs, ks, vs = (split_cp_2d(a, frames, height, width, split_h, split_w) for a in (q, k, v))
+    qh, kh, vh = (send_recv_heads(a) for a in (qs, ks, vs))
+    oh = np.stack([attention_heads(qh[r], kh[r], vh[r], scale, None, None) for r in range(n_ranks)])
+    return gather_cp_2d(gather_heads(oh), frames, height, width, split_h, split_w)
 
 
 def reference_attention(q, k, v, scale: float, user_mask=None, kv_valid_len=None):

@@ -322,3 +322,70 @@ def check_joint_av_block(O):
         ref = O.reference_attention(x["q"], x["k"], x["v"], 1.0 / np.sqrt(x["q"].shape[-1]))
         assert out[name].shape == x["q"].shape, name
         assert np.max(np.abs(out[name] - ref)) < 1e-12, name
+
+
+def check_split_2d_golden(O):
+    """The hand-worked 2-D split ([LC] 智能张量拆分策略)."""
+    from tests.conftest import load_golden
+    g = load_golden("split_2d_F2_H2_W4_N4.txt")
+    sh, sw = O.get_optimal_split(g["n_ranks"], g["height"], g["width"])
+    assert [sh, sw] == g["split"]
+    t = g["frames"] * g["height"] * g["width"]
+    x = np.arange(t, dtype=np.int64).reshape(1, t)
+    tiles = O.split_cp_2d(x, g["frames"], g["height"], g["width"], sh, sw)
+    assert tiles.tolist() == g["tiles"]
+    assert O.gather_cp_2d(tiles, g["frames"], g["height"], g["width"], sh, sw).tolist() == x.tolist()
+
+
+def check_optimal_split(O):
+    """Closed forms of the near-square choice (R17), and its error."""
+    assert O.get_optimal_split(8, 16, 24) == (2, 4)      # 8 x 6 tiles beat 4 x 12
+    assert O.get_optimal_split(8, 64, 64) == (2, 4)      # tie of orientations -> smaller split_h
+    assert O.get_optimal_split(1, 5, 7) == (1, 1)
+    assert O.get_optimal_split(7, 7, 5) == (7, 1)        # a prime: the only even split
+    assert O.get_optimal_split(6, 6, 4) == (3, 2)        # 2 x 3 does not divide the width
+    assert O.get_optimal_split(16, 32, 32) == (4, 4)
+    for args in [(8, 3, 5), (0, 4, 4)]:
+        try:
+            O.get_optimal_split(*args)
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"get_optimal_split{args} must raise")
+
+
+def check_split_2d_brute_force(O):
+    """Element loops in pure Python == split_cp_2d; every token lands exactly
+    once; gather_cp_2d returns the input byte for byte."""
+    rng = np.random.default_rng(18)
+    for (b, f, hh, ww, n, c) in [(1, 2, 4, 6, 6, 3), (2, 3, 6, 4, 4, 2), (1, 1, 8, 8, 8, 1)]:
+        sh, sw = O.get_optimal_split(n, hh, ww)
+        th, tw = hh // sh, ww // sw
+        x = rng.integers(0, 1 << 30, size=(b, f * hh * ww, c)).astype(np.int64)
+        tiles = O.split_cp_2d(x, f, hh, ww, sh, sw)
+        seen = np.zeros(f * hh * ww, dtype=np.int64)
+        for r in range(n):
+            i, j = divmod(r, sw)
+            for bb in range(b):
+                lt = 0
+                for ff in range(f):
+                    for y in range(th):
+                        for xx in range(tw):
+                            t = ff * hh * ww + (i * th + y) * ww + (j * tw + xx)
+                            assert (tiles[r, bb, lt] == x[bb, t]).all()
+                            if bb == 0:
+                                seen[t] += 1
+                            lt += 1
+        assert (seen == 1).all()
+        back = O.gather_cp_2d(tiles, f, hh, ww, sh, sw)
+        assert back.tobytes() == x.tobytes()
+
+
+def check_sharded_equals_unsharded_2d(O):
+    """2-D split, exchange, attention, exchange back, gather: unsharded attention."""
+    rng = np.random.default_rng(19)
+    for (b, f, hh, ww, n, h, d) in [(1, 2, 4, 6, 8, 8, 4), (2, 1, 6, 6, 4, 4, 3)]:
+        t = f * hh * ww
+        q, k, v = (rng.standard_normal((b, t, h, d)) for _ in range(3))
+        got = O.ulysses_self_attention_2d(q, k, v, f, hh, ww, n, 0.4)
+        assert np.max(np.abs(got - O.reference_attention(q, k, v, 0.4))) < 1e-12

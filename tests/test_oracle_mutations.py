@@ -19,7 +19,8 @@ CHECKS = [
     P.check_attention_closed_forms, P.check_garbage_pad_invariance, P.check_gather_output,
     P.check_sharded_equals_unsharded_self, P.check_sharded_equals_unsharded_mask,
     P.check_sharded_equals_unsharded_cross, P.check_attention_sdpa, P.check_cross_query_padding,
-    P.check_joint_av_block,
+    P.check_joint_av_block, P.check_split_2d_golden, P.check_optimal_split, P.check_split_2d_brute_force,
+    P.check_sharded_equals_unsharded_2d,
 ]
 
 MUTANTS = {
@@ -45,6 +46,11 @@ MUTANTS = {
                                              "attention_heads(q[:, :, 0:hl], kh[r]"),
     "user mask rows/cols transposed": ("out[:, :t, :t] = (m != 0)", "out[:, :t, :t] = (m != 0).transpose(0, 2, 1)"),
     "cross: query padding ignored": ("q = pad_tokens(q, tq_pad)", "q = q"),
+    "2-D: ranks numbered column-major": ("r = i * split_w + j\n            grid[", "r = j * split_h + i\n            grid["),
+    "2-D: split ratio farthest from square": ("key = (abs(a - b), abs(height // a - width // b), a)",
+                                             "key = (-abs(a - b), abs(height // a - width // b), a)"),
+    "2-D: tile ignores the frames": ("tile = grid[:, :, i * th:(i + 1) * th, j * tw:(j + 1) * tw]",
+                                     "tile = grid[:, :1, i * th:(i + 1) * th, j * tw:(j + 1) * tw]"),
     "joint: cross keys from the wrong modality": ('(("v2a", audio_tokens, ta_pad, tv_pad),',
                                                  '(("v2a", video_tokens, tv_pad, tv_pad),'),
 }

@@ -153,3 +153,19 @@ def test_cross_query_padding():
 
 def test_joint_av_block():
     P.check_joint_av_block(O)
+
+
+def test_split_2d_golden():
+    P.check_split_2d_golden(O)
+
+
+def test_optimal_split():
+    P.check_optimal_split(O)
+
+
+def test_split_2d_brute_force():
+    P.check_split_2d_brute_force(O)
+
+
+def test_sharded_equals_unsharded_2d():
+    P.check_sharded_equals_unsharded_2d(O)
