@@ -208,7 +208,7 @@ def main():
 
     from sequence_attention_video_amd import binding
     from sequence_attention_video_amd.pipeline import UlyssesStep
-    from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
+    from sequence_attention_video_amd.workloads import GRIDS, WORKLOADS, make_inputs
 
     binding.load()          # fails loudly if the HIP library is missing
     if args.config == "joint_av":
@@ -304,6 +304,35 @@ def main():
     zero_equal = bool(torch.equal(step.outz.view(torch.uint8), ref_out.view(torch.uint8)))
     del ref_out
 
+    # -- the 2-D (height x width) split in place of the 1-D token split, for
+    #    workloads that are one video grid; reported beside the step
+    cp2d = None
+    if args.config in GRIDS:
+        from sequence_attention_video_amd.pipeline import Ulysses2DStep
+        step2 = Ulysses2DStep(wl, GRIDS[args.config], q, k, v, device=dev)
+        for _ in range(max(3, args.warmup // 4)):
+            step2.run()
+        c0 = torch.cuda.Event(enable_timing=True)
+        c1 = torch.cuda.Event(enable_timing=True)
+        c2 = torch.cuda.Event(enable_timing=True)
+        c0.record(stream)
+        for _ in range(args.steps):
+            step2.run()
+        c1.record(stream)
+        for _ in range(args.steps):
+            step2.split_cp_2d()
+        c2.record(stream)
+        torch.cuda.synchronize()
+        ms_2d = c0.elapsed_time(c1) / args.steps
+        ms_tile = c1.elapsed_time(c2) / args.steps
+        tile_bytes = 2 * 3 * B * T * H * D * eb
+        cp2d = {"ms": round(ms_2d, 4), "TFLOP/s": round(attn_flops / (ms_2d * 1e-3) / 1e12, 2),
+                "split_hw": list(step2.split), "grid_fhw": list(GRIDS[args.config]),
+                "split_cp_2d_qkv": {"ms": round(ms_tile, 4), "bytes": tile_bytes,
+                                    "GB/s": round(tile_bytes / (ms_tile * 1e-3) / 1e9, 1)},
+                "max_abs_diff_vs_step": float((step2.out.float() - step.out.float()).abs().max().item())}
+        del step2
+
     # -- relayout bandwidth with rotating buffer sets (> 1 GB in flight defeats the 256 MB MALL)
     set_bytes = relayout_bytes
     nsets = max(2, int(math.ceil(1.2e9 / max(set_bytes, 1))))
@@ -392,6 +421,7 @@ def main():
                          "GB/s": round(gbs(relayout_o_bytes, ms_gh), 1)},
         "gather_output_tokens": {"ms": round(ms_gather, 4), "bytes": gather_bytes,
                                  "GB/s": round(gbs(gather_bytes, ms_gather), 1)},
+        "cp2d_step": cp2d,
         "zero_copy_step": {"ms": round(ms_zero, 4), "TFLOP/s": round(attn_flops / (ms_zero * 1e-3) / 1e12, 2),
                            "output_bytes_equal_to_step": zero_equal},
         "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),

@@ -184,6 +184,49 @@ sp_status sp_gather_unpad(const void* in, sp_shard_strides in_strides, void* out
                           int64_t Ts, int64_t C, const int64_t* counts, int64_t T, sp_dtype dtype,
                           void* stream);
 
+/* Direction of sp_tile_2d. */
+typedef enum {
+  SP_GRID_TO_TILES = 0, /* split_cp_2d: the token grid -> every rank's tile */
+  SP_TILES_TO_GRID = 1  /* gather_cp_2d: the inverse */
+} sp_tile_dir;
+
+/*
+ * sp_optimal_split -- the rank grid of the 2-D (height x width) split
+ * ([LC] "LongCat-Video上下文并行技术如何实现高效的多GPU推理", section
+ * 智能张量拆分策略: the split ratio closest to a square).  Host only.
+ * Among factor pairs split_h * split_w = n_ranks with height % split_h == 0
+ * and width % split_w == 0: the pair closest to square (smallest
+ * |split_h - split_w|), then the orientation whose tiles are closer to square
+ * (smallest |height/split_h - width/split_w|), then the smaller split_h.
+ * split_h, split_w: host outputs (either may be NULL).
+ * Errors: n_ranks < 1, height or width < 1 -> SP_ERR_INVALID_ARG; no even
+ * split -> SP_ERR_NOT_DIVISIBLE.
+ */
+sp_status sp_optimal_split(int32_t n_ranks, int64_t height, int64_t width, int32_t* split_h, int32_t* split_w);
+
+/*
+ * sp_tile_2d -- the 2-D split of a token grid over split_h x split_w ranks and
+ * its inverse ([LC] 智能张量拆分策略: split_tensor_in_cp_2d splits along height
+ * then width; gather_cp_2d puts the pieces back).  A bit copy.
+ * grid: (B, F, height, width, C) tokens in raster order (token f*height*width
+ *   + y*width + x), batch b at grid + b*grid_batch_stride, rows of C packed.
+ * tiles: rank r = i*split_w + j, batch b at tiles + r*tiles.rank +
+ *   b*tiles.batch: F*th*tw rows of C packed (th = height/split_h, tw =
+ *   width/split_w): rows i*th.., columns j*tw.. of every frame, in raster
+ *   order within the tile.
+ * SP_GRID_TO_TILES reads grid (src) and writes tiles (dst); SP_TILES_TO_GRID
+ * the reverse.  All strides in elements; the round trip returns the input
+ * byte for byte.
+ * Errors: height % split_h or width % split_w != 0 -> SP_ERR_NOT_DIVISIBLE;
+ * negative sizes, split < 1, null, misaligned (16 bytes) or overlapping
+ * pointers, tile blocks that overlap, grid_batch_stride < F*height*width*C ->
+ * SP_ERR_INVALID_ARG; C * element size not a multiple of 16 bytes, more than
+ * 65535 rank x batch blocks -> SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_tile_2d(const void* src, void* dst, int32_t split_h, int32_t split_w, int64_t B, int64_t F,
+                     int64_t height, int64_t width, int64_t C, sp_dtype dtype, sp_tile_dir dir,
+                     sp_shard_strides tiles, int64_t grid_batch_stride, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,11 +20,13 @@ LIB_PATH = os.path.join(PKG, "libspattn.so")
 SP_OK, SP_ERR_NOT_DIVISIBLE, SP_ERR_INVALID_ARG, SP_ERR_UNSUPPORTED, SP_ERR_HIP = range(5)
 SP_F32, SP_BF16 = 0, 1
 SP_TOKENS_TO_HEADS, SP_HEADS_TO_TOKENS = 0, 1
+SP_GRID_TO_TILES, SP_TILES_TO_GRID = 0, 1
 
 # names declared in include/sp.h (checked against the header by the tests)
 EXPORTS = (
     "sp_status_string", "sp_version", "sp_partition", "sp_pad", "sp_relayout_heads",
-    "sp_masked_attention_workspace_size", "sp_masked_attention", "sp_gather_unpad",
+    "sp_masked_attention_workspace_size", "sp_masked_attention", "sp_gather_unpad", "sp_optimal_split",
+    "sp_tile_2d",
 )
 
 
@@ -74,6 +76,11 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sp_gather_unpad.restype = ctypes.c_int
     lib.sp_gather_unpad.argtypes = [vp, ShardStrides, vp, i32, i64, i64, i64, ctypes.POINTER(i64), i64,
                                     ctypes.c_int, vp]
+    lib.sp_optimal_split.restype = ctypes.c_int
+    lib.sp_optimal_split.argtypes = [i32, i64, i64, ctypes.POINTER(i32), ctypes.POINTER(i32)]
+    lib.sp_tile_2d.restype = ctypes.c_int
+    lib.sp_tile_2d.argtypes = [vp, vp, i32, i32, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
+                               ShardStrides, i64, vp]
     if path is None:
         _lib = lib
     return lib
@@ -217,3 +224,24 @@ def sp_gather_unpad(inp, out, W: int, B: int, Ts: int, C: int, T: int, counts=No
         carr = (ctypes.c_int64 * len(counts))(*[int(c) for c in counts])
     check(load().sp_gather_unpad(_ptr(inp), ShardStrides(*st), _ptr(out), int(W), int(B), int(Ts), int(C),
                                  carr, int(T), _dtype_code(inp), _stream(stream)))
+
+
+def sp_optimal_split(n_ranks: int, height: int, width: int):
+    """(split_h, split_w): the near-square rank grid of the 2-D split."""
+    a, b = ctypes.c_int32(0), ctypes.c_int32(0)
+    check(load().sp_optimal_split(int(n_ranks), int(height), int(width), ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def sp_tile_2d(src, dst, split_h: int, split_w: int, B: int, F: int, height: int, width: int, C: int,
+               direction: int, tile_strides=None, grid_batch_stride=None, stream=None):
+    """split_cp_2d (SP_GRID_TO_TILES) or gather_cp_2d (SP_TILES_TO_GRID) on one device.
+    Grid side (B, F*height*width, C); tile side (N, B, F*th*tw, C) stacked unless strides are given."""
+    _cuda(src, dst)
+    grid = src if direction == SP_GRID_TO_TILES else dst
+    tt = F * (height // split_h) * (width // split_w)
+    ts = tile_strides or (B * tt * C, tt * C)
+    gbs = grid_batch_stride if grid_batch_stride is not None else F * height * width * C
+    check(load().sp_tile_2d(_ptr(src), _ptr(dst), int(split_h), int(split_w), int(B), int(F), int(height),
+                            int(width), int(C), _dtype_code(grid), int(direction), ShardStrides(*ts), int(gbs),
+                            _stream(stream)))

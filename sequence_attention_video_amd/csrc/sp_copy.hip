@@ -85,6 +85,58 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 2-D tiles
+
+struct Tile2dArgs {
+  const char* src;
+  char* dst;
+  int64_t B;
+  int64_t grid_batch_b, row_b;        // grid side (bytes)
+  int64_t tile_rank_b, tile_batch_b;  // tile side (bytes)
+  int64_t height, width, th, tw;
+  int32_t split_w;
+  uint32_t runV;                      // 16-byte vectors of one tile row run (tw tokens)
+  FastDiv fd_runV, fd_th;
+  uint32_t n_per_rb;                  // F*th*runV vectors per (rank, batch)
+  uint32_t chunks;                    // workgroups per (rank, batch)
+  int to_tiles;                       // 1: grid -> tiles
+};
+
+// blockIdx.x = chunk, blockIdx.y = (rank r, batch b).  On the tile side the
+// block (r, b) is contiguous; on the grid side it is F*th runs of tw whole
+// token rows (one frame row of the tile), each contiguous.  Flat vector f of
+// the block is run f / runV (frame f_ = run / th, tile row y = run % th),
+// vector f % runV of the run.
+__global__ __launch_bounds__(kThreads) void tile_2d_kernel(Tile2dArgs a) {
+  const int64_t r = blockIdx.y / a.B;
+  const int64_t b = blockIdx.y - r * a.B;
+  const int64_t i = r / a.split_w, j = r - (r / a.split_w) * a.split_w;
+  const int64_t tile_off = r * a.tile_rank_b + b * a.tile_batch_b;
+  const int64_t grid_off = b * a.grid_batch_b + (i * a.th * a.width + j * a.tw) * a.row_b;
+  vec16 buf[kUnroll];
+  int64_t waddr[kUnroll];
+  const uint32_t f0 = blockIdx.x * uint32_t(kChunk) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_rb) {
+      const uint32_t run = fdiv(f, a.fd_runV);
+      const uint32_t v = f - run * a.runV;
+      const uint32_t fr = fdiv(run, a.fd_th);
+      const uint32_t y = run - fr * uint32_t(a.th);
+      const int64_t g = grid_off + ((int64_t(fr) * a.height + y) * a.width) * a.row_b + int64_t(v) * 16;
+      const int64_t t = tile_off + int64_t(f) * 16;
+      waddr[u] = a.to_tiles ? t : g;
+      buf[u] = load16(a.src + (a.to_tiles ? g : t));
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_rb) store16(a.dst + waddr[u], buf[u]);
+  }
+}
+
 // ------------------------------------------------------------------ pad
 
 struct PadArgs {
@@ -414,5 +466,54 @@ extern "C" sp_status sp_gather_unpad(const void* in, sp_shard_strides in_strides
   }
   dim3 grid(unsigned(div_up(max_vec, kChunk)), unsigned(W * B));
   hipLaunchKernelGGL(gather_unpad_kernel, grid, dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" sp_status sp_tile_2d(const void* src, void* dst, int32_t split_h, int32_t split_w, int64_t B, int64_t F,
+                                int64_t height, int64_t width, int64_t C, sp_dtype dtype, sp_tile_dir dir,
+                                sp_shard_strides tiles, int64_t grid_batch_stride, void* stream) {
+  if (!dtype_ok(dtype) || (dir != SP_GRID_TO_TILES && dir != SP_TILES_TO_GRID)) return SP_ERR_INVALID_ARG;
+  if (split_h < 1 || split_w < 1 || B < 0 || F < 0 || height < 0 || width < 0 || C < 0) return SP_ERR_INVALID_ARG;
+  if (height % split_h != 0 || width % split_w != 0) return SP_ERR_NOT_DIVISIBLE;
+  const int64_t eb = elem_bytes(dtype);
+  if ((C * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  const int64_t N = int64_t(split_h) * split_w;
+  const int64_t th = height / split_h, tw = width / split_w;
+  const int64_t T = F * height * width, Tt = F * th * tw;
+  if (B == 0 || T == 0 || C == 0) return SP_OK;
+  if (src == nullptr || dst == nullptr || src == dst) return SP_ERR_INVALID_ARG;
+  if (!aligned16(src) || !aligned16(dst)) return SP_ERR_INVALID_ARG;
+  if (grid_batch_stride < T * C || (grid_batch_stride * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  if ((tiles.rank * eb) % 16 != 0 || (tiles.batch * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  if (!disjoint_blocks(tiles.rank, tiles.batch, N, B, Tt * C)) return SP_ERR_INVALID_ARG;
+  // the two sides must not overlap
+  const void* grid = dir == SP_GRID_TO_TILES ? src : dst;
+  const void* tl = dir == SP_GRID_TO_TILES ? dst : src;
+  const char* gs = static_cast<const char*>(grid);
+  const char* ts = static_cast<const char*>(tl);
+  const char* ge = gs + ((B - 1) * grid_batch_stride + T * C) * eb;
+  const char* te = ts + ((N - 1) * tiles.rank + (B - 1) * tiles.batch + Tt * C) * eb;
+  if (gs < te && ts < ge) return SP_ERR_INVALID_ARG;
+  if (N * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  const int64_t runV = tw * C * eb / 16;
+  const int64_t n_per_rb = F * th * runV;
+  if (n_per_rb >= (int64_t(1) << 32) - kChunk) return SP_ERR_UNSUPPORTED;
+  Tile2dArgs a;
+  a.src = static_cast<const char*>(src);
+  a.dst = static_cast<char*>(dst);
+  a.B = B;
+  a.grid_batch_b = grid_batch_stride * eb;
+  a.row_b = C * eb;
+  a.tile_rank_b = tiles.rank * eb;
+  a.tile_batch_b = tiles.batch * eb;
+  a.height = height; a.width = width; a.th = th; a.tw = tw;
+  a.split_w = split_w;
+  a.runV = uint32_t(runV);
+  a.fd_runV = make_fastdiv(uint32_t(runV));
+  a.fd_th = make_fastdiv(uint32_t(th));
+  a.n_per_rb = uint32_t(n_per_rb);
+  a.chunks = uint32_t(div_up(n_per_rb, kChunk));
+  a.to_tiles = dir == SP_GRID_TO_TILES;
+  hipLaunchKernelGGL(tile_2d_kernel, dim3(a.chunks, unsigned(N * B)), dim3(kThreads), 0, as_stream(stream), a);
   return launch_status();
 }

@@ -32,3 +32,30 @@ extern "C" sp_status sp_partition(int64_t total_tokens, int32_t world_size, int6
   }
   return SP_OK;
 }
+
+// get_optimal_split: page "LongCat-Video上下文并行技术如何实现高效的多GPU推理",
+// section 智能张量拆分策略 -- the split of the height x width grid over the
+// ranks whose ratio is closest to a square; an uneven split is not offered.
+extern "C" sp_status sp_optimal_split(int32_t n_ranks, int64_t height, int64_t width, int32_t* split_h,
+                                      int32_t* split_w) {
+  if (n_ranks < 1 || height < 1 || width < 1) return SP_ERR_INVALID_ARG;
+  int32_t best_a = 0;
+  int64_t best_k0 = 0, best_k1 = 0;
+  for (int32_t a = 1; a <= n_ranks; ++a) {
+    if (n_ranks % a != 0) continue;
+    const int32_t b = n_ranks / a;
+    if (height % a != 0 || width % b != 0) continue;
+    const int64_t k0 = a > b ? a - b : b - a;                       // ranks closest to square
+    const int64_t th = height / a, tw = width / b;
+    const int64_t k1 = th > tw ? th - tw : tw - th;                 // then tiles closest to square
+    if (best_a == 0 || k0 < best_k0 || (k0 == best_k0 && k1 < best_k1)) {   // ties keep the smaller a
+      best_a = a;
+      best_k0 = k0;
+      best_k1 = k1;
+    }
+  }
+  if (best_a == 0) return SP_ERR_NOT_DIVISIBLE;
+  if (split_h) *split_h = best_a;
+  if (split_w) *split_w = n_ranks / best_a;
+  return SP_OK;
+}

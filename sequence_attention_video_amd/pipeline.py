@@ -246,3 +246,71 @@ class JointAVStep:
 
     def run(self) -> dict:
         return {name: self.steps[name].run() for name in self.PARTS}
+
+
+class Ulysses2DStep:
+    """Self-attention with the 2-D (height x width) split of page
+    "LongCat-Video上下文并行技术如何实现高效的多GPU推理" (section 智能张量拆分策略)
+    in place of the 1-D token split: the W ranks form a near-square
+    split_h x split_w grid over the latent's height x width (sp_optimal_split);
+    split_cp_2d gives each rank its tile of every frame (sp_tile_2d), the head
+    exchange, attention and the way back run as in UlyssesStep on those
+    shards, and gather_cp_2d (sp_tile_2d) restores raster order.  Attention
+    does not depend on token order (key-only mask, no padding: the grid must
+    split evenly), so the output is the same attention up to summation order.
+    Memory: tiles (W, B, Tt, H, D) with Tt = F*th*tw; head side
+    (W, B, T, Hl, D) in rank-then-tile token order."""
+
+    def __init__(self, wl: Workload, grid, q, k, v, device="cuda"):
+        self.wl = wl
+        F, Hh, Ww = grid
+        if F * Hh * Ww != wl.T or wl.T_pad != wl.T:
+            raise ValueError("the grid must hold exactly the workload's tokens")
+        self.grid = grid
+        B, H, D, W, T, Hl = wl.B, wl.H, wl.D, wl.W, wl.T, wl.Hl
+        self.split = sp.sp_optimal_split(W, Hh, Ww)
+        self.Tt = T // W
+        dt = TORCH_DTYPE[wl.dtype]
+        e = lambda *s: torch.empty(*s, dtype=dt, device=device)
+        self.q, self.k, self.v = q, k, v
+        self.qt, self.kt, self.vt = (e(W, B, self.Tt, H, D) for _ in range(3))
+        self.qh, self.kh, self.vh = (e(W, B, T, Hl, D) for _ in range(3))
+        self.oh = e(W, B, T, Hl, D)
+        self.ot = e(W, B, self.Tt, H, D)
+        self.out = e(B, T, H, D)
+        self.scale = 1.0 / math.sqrt(D)
+
+    def split_cp_2d(self):
+        wl = self.wl
+        F, Hh, Ww = self.grid
+        for x, y in ((self.q, self.qt), (self.k, self.kt), (self.v, self.vt)):
+            sp.sp_tile_2d(x, y, *self.split, wl.B, F, Hh, Ww, wl.H * wl.D, sp.SP_GRID_TO_TILES)
+
+    def send_recv_heads(self):
+        wl = self.wl
+        sp.sp_relayout_heads([self.qt, self.kt, self.vt], [self.qh, self.kh, self.vh], wl.W, wl.B, wl.T, wl.H,
+                             wl.D, sp.SP_TOKENS_TO_HEADS)
+
+    def attention(self):
+        wl = self.wl
+        B, T, Hl, D = wl.B, wl.T, wl.Hl, wl.D
+        hs = (B * T * Hl * D, T * Hl * D, Hl * D, D)
+        sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, T, T, Hl, D, hs, hs, hs, hs,
+                               kv_valid_len=T, scale=self.scale)
+
+    def gather_heads(self):
+        wl = self.wl
+        sp.sp_relayout_heads([self.oh], [self.ot], wl.W, wl.B, wl.T, wl.H, wl.D, sp.SP_HEADS_TO_TOKENS)
+
+    def gather_cp_2d(self):
+        wl = self.wl
+        F, Hh, Ww = self.grid
+        sp.sp_tile_2d(self.ot, self.out, *self.split, wl.B, F, Hh, Ww, wl.H * wl.D, sp.SP_TILES_TO_GRID)
+
+    def run(self):
+        self.split_cp_2d()
+        self.send_recv_heads()
+        self.attention()
+        self.gather_heads()
+        self.gather_cp_2d()
+        return self.out

@@ -118,6 +118,10 @@ class JointWorkload:
         }
 
 
+# latent grids (frames, height, width) of the workloads whose tokens are one
+# video: 16 frames of 16 x 24 (video_self), 8 frames of 64 x 64 (long_hires)
+GRIDS = {"video_self": (16, 16, 24), "long_hires": (8, 64, 64)}
+
 JOINT_AV = JointWorkload()
 JOINT_SEED_OFFSET = {"video_self": 0, "audio_self": 10, "v2a": 20, "a2v": 30}
 

@@ -189,3 +189,52 @@ def test_bench_refuses_more_than_one_gpu():
                          capture_output=True, text=True, timeout=120)
     assert res.returncode == 2
     assert "one GPU" in res.stderr and res.stdout == ""
+
+
+def test_optimal_split_matches_oracle(lib):
+    """The library's near-square split (host code) against the oracle's, over
+    every rank count up to 16 and small grids, errors included."""
+    import oracle as O
+    from sequence_attention_video_amd import binding as b
+    for n in range(1, 17):
+        for h in range(1, 13):
+            for w in range(1, 13):
+                try:
+                    want = O.get_optimal_split(n, h, w)
+                except ValueError:
+                    want = None
+                if want is None:
+                    with pytest.raises(ValueError):
+                        b.sp_optimal_split(n, h, w)
+                else:
+                    assert b.sp_optimal_split(n, h, w) == want, (n, h, w)
+    assert b.sp_optimal_split(8, 16, 24) == (2, 4)
+    assert b.sp_optimal_split(8, 64, 64) == (2, 4)
+    assert lib.sp_optimal_split(0, 4, 4, None, None) == b.SP_ERR_INVALID_ARG
+
+
+def test_tile_2d_validation(lib):
+    from sequence_attention_video_amd import binding as b
+    S = b.ShardStrides
+    C = 4096
+    src, dst = ctypes.c_void_p(1 << 40), ctypes.c_void_p(2 << 40)
+    st = S(6144 * C, 768 * C)
+    # height not divisible by split_h
+    assert lib.sp_tile_2d(src, dst, 3, 4, 1, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, st, 6144 * C,
+                          None) == b.SP_ERR_NOT_DIVISIBLE
+    # row not a multiple of 16 bytes; bad direction; overlapping sides; null pointer
+    assert lib.sp_tile_2d(src, dst, 2, 4, 1, 16, 16, 24, 3, b.SP_BF16, b.SP_GRID_TO_TILES, S(768 * 3, 768 * 3),
+                          6144 * 3, None) == b.SP_ERR_UNSUPPORTED
+    assert lib.sp_tile_2d(src, dst, 2, 4, 1, 16, 16, 24, C, b.SP_BF16, 7, st, 6144 * C, None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_tile_2d(src, ctypes.c_void_p((1 << 40) + 4096), 2, 4, 1, 16, 16, 24, C, b.SP_BF16,
+                          b.SP_GRID_TO_TILES, st, 6144 * C, None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_tile_2d(None, dst, 2, 4, 1, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, st, 6144 * C,
+                          None) == b.SP_ERR_INVALID_ARG
+    # tile blocks that overlap each other; grid batch stride too small
+    assert lib.sp_tile_2d(src, dst, 2, 4, 2, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, S(768 * C, 100),
+                          6144 * C, None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_tile_2d(src, dst, 2, 4, 2, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, S(2 * 768 * C, 768 * C),
+                          6000 * C, None) == b.SP_ERR_INVALID_ARG
+    # nothing to copy is a no-op
+    assert lib.sp_tile_2d(None, None, 2, 4, 0, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, st, 6144 * C,
+                          None) == b.SP_OK
