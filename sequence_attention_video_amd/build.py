@@ -25,8 +25,12 @@ SOURCES = ["sp_host.cpp", "sp_copy.hip", "sp_attention.hip"]
 ARCH = "gfx950"
 # Per-source compiler options.  The attention kernel keeps its MFMA results in
 # architectural VGPRs: the softmax reads them with VALU instructions, and the
-# default heuristic (AGPR results) costs a copy per element per tile.
-EXTRA_FLAGS = {"sp_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+# default heuristic (AGPR results) costs a copy per element per tile.  Its
+# machine scheduler uses the memory-clause strategy with the target's own
+# register-pressure trackers (measured 0.5-1 % faster on every workload).
+EXTRA_FLAGS = {"sp_attention.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form",
+                                    "-mllvm", "-amdgpu-sched-strategy=max-memory-clause",
+                                    "-mllvm", "-amdgpu-use-amdgpu-trackers"]}
 
 
 def hipcc() -> str:
