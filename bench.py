@@ -37,10 +37,16 @@ def log(*a):
 
 
 def kernel_hash(*names) -> str:
+    """Hash of the named kernel sources and of the compiler flags they are
+    built with (build.py), so that a profile taken on other code or flags is
+    never reported as current."""
+    from sequence_attention_video_amd import build as b
     h = hashlib.sha256()
     for n in names:
         with open(os.path.join(ROOT, "sequence_attention_video_amd", "csrc", n), "rb") as f:
             h.update(f.read())
+        flags = [f for f in b.compile_flags() + b.EXTRA_FLAGS.get(n, []) if not os.path.isabs(f)]
+        h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
 
 
