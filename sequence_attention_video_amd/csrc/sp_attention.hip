@@ -35,10 +35,12 @@
 //     between rescales; row sums add the bf16-rounded p with v_dot2;
 //   * user masks are classified once per call into empty/full/partial tiles:
 //     empty tiles are skipped, full tiles read no mask bytes, partial tiles one
-//     64-bit visibility word per row and 64 keys;
-//   * workgroup ids are remapped so that the 8 XCDs each take a contiguous run
-//     of (rank, batch, head) groups: the q-tiles sharing one head's K/V run on
-//     the same XCD and share its L2;
+//     64-bit visibility word per row and 64 keys (loaded a tile ahead; the
+//     tile classes of a query tile's row sit in LDS);
+//   * without a user mask, workgroup ids are remapped so that the 8 XCDs each
+//     take a contiguous run of (rank, batch, head) groups: the q-tiles sharing
+//     one head's K/V run on the same XCD and share its L2; with a user mask
+//     the work is uneven and query tiles go longest first over the whole GPU;
 //   * launches with too few query tiles to fill the GPU (one rank's share)
 //     split the key range over all compute units and merge partial results
 //     (attn_combine_kernel).
@@ -150,10 +152,6 @@ __device__ __forceinline__ float wave_max_pair(float x) {
 }
 
 // ---------------------------------------------------------------- bf16 kernel
-
-// Waits until this wave's direct global->LDS loads have landed (vmcnt = 0; the
-// expcnt and lgkmcnt fields are left at their maximum, i.e. not waited on).
-__device__ __forceinline__ void wait_vmem() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS layout of one K or V tile (KT keys x D dims, bf16).  The tile is cut
 // into groups of KPG keys whose rows make exactly 1 KiB (KPG = 4 at D = 128,
