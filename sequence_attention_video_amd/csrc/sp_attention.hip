@@ -8,12 +8,12 @@
 // keys visible).
 //
 // Design (bf16):
-//   * one workgroup = 8 waves = 256 query rows of one (rank, batch, head); each
-//     wave owns 32 query rows for the whole key loop, and two waves share each
-//     SIMD, so one wave's softmax (VALU) runs while the other's MFMAs do.  The
-//     kernel is templated on query blocks per wave (QB); two blocks per wave
-//     would let every LDS operand feed two MFMAs, but at D = 128 the registers
-//     then only allow one wave per SIMD, which measured slower;
+//   * one workgroup = 12 waves = 384 query rows of one (rank, batch, head);
+//     each wave owns 32 query rows for the whole key loop, and three waves
+//     share each SIMD, so one wave's softmax (VALU) runs while another's MFMAs
+//     do.  The kernel is templated on query blocks per wave (QB); two blocks
+//     per wave would let every LDS operand feed two MFMAs, but at D = 128 the
+//     registers then only allow one wave per SIMD, which measured slower;
 //   * key tiles of KT = 128 are fetched with 16-byte MUBUF loads straight into
 //     LDS (double buffer, one barrier per tile; the next tile's loads overlap
 //     this tile's compute); the tile is stored as padded 1 KiB key groups (see
@@ -54,7 +54,13 @@ namespace sp {
 namespace {
 
 constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
-constexpr int BF16_WAVES = 8;        // waves per bf16 workgroup
+// Waves per bf16 workgroup: 12, three per SIMD (measured +4-6 % over 8).  At
+// three waves the D = 128 kernels sit at the 168-VGPR limit and the compiler
+// spills a few 64-bit values of the edge-tile load path to scratch (reloaded
+// once per query tile, outside the per-part work); after any change, check
+// that no scratch access lands in the per-tile path (the tile loop's load
+// issue and compute blocks), which costs 5-10 %.
+constexpr int BF16_WAVES = 12;
 constexpr int BF16_THREADS = 64 * BF16_WAVES;
 constexpr int BM = 32 * QB * BF16_WAVES;   // query rows per bf16 workgroup, and the mask-class tile height
 constexpr int BM32 = 128;            // query rows per fp32 workgroup
@@ -917,19 +923,21 @@ int64_t device_cus() {
   return n;
 }
 
-// Split decision for the bf16 kernel without a user mask (one workgroup per CU
-// fits in LDS): with `items` query tiles of nku key tiles each, a plain launch
-// takes ceil(items / ncu) * nku tile-times; a split launch takes upw =
-// ceil(items * nku / ncu) plus about four for writing the partial records and
-// the merge launch (measured on MI355X: 3-4 us per tile-time at D = 128, about
-// 20 us for the records of a 4-head, 6144-token share).  Returns upw when the
-// split pays by 1.3x, else 0.
-int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu) {
+// Split decision for the bf16 kernel (one workgroup per CU fits in LDS): with
+// `items` query tiles of nku key tiles each, a plain launch takes
+// ceil(items / ncu) * nku tile-times; a split launch takes upw =
+// ceil(items * nku / ncu) plus a fixed cost for the partial records and the
+// merge launch, about 4 tile-times at D = 128 and twice that at D = 64 (a
+// tile costs half as much; measured on MI355X: ~4 us per tile-time at
+// D = 128, ~15 us of fixed cost).  Returns upw when the split pays by 1.3x,
+// else 0.
+int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D) {
   if (items <= 0 || nku < 2 || ncu <= 0) return 0;
   const int64_t upw = div_up(items * nku, ncu);
   if (upw >= nku) return 0;
   const int64_t plain = div_up(items, ncu) * nku;
-  return plain * 10 >= (upw + 4) * 13 ? upw : 0;
+  const int64_t fixed = 4 * 128 / D;
+  return plain * 10 >= (upw + fixed) * 13 ? upw : 0;
 }
 
 // bytes of partial records of a split launch: two slots per workgroup
@@ -958,7 +966,7 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   if (dtype == SP_BF16 && (D == 64 || D == 128)) {
     const int64_t ncu = device_cus();
     const int64_t items = div_up(Tq, BM) * Hl * B * R;
-    if (split_units_per_wg(items, div_up(Tk, KT), ncu)) split = split_bytes(ncu, D);
+    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D)) split = split_bytes(ncu, D);
   }
   return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
 }
@@ -1024,7 +1032,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (dtype == SP_BF16) {
     const int64_t ncu = device_cus();
     const int64_t nku = div_up(a.kv_end, KT);
-    const int64_t upw = split_units_per_wg(nwg, nku, ncu);
+    const int64_t upw = split_units_per_wg(nwg, nku, ncu, D);
     // the split runs only with room for its partial records after the mask
     // part (as sized by sp_masked_attention_workspace_size); otherwise the
     // plain launch runs

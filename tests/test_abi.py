@@ -123,18 +123,18 @@ def test_validation_returns_before_launch(lib):
 def test_workspace_size(lib):
     from sequence_attention_video_amd import binding as b
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == 0
-    # one class byte per (256-row, 64-key) tile of the mask, padded to 256 bytes,
-    # then one 64-bit word per mask row and 64-key tile
+    # one class byte per (384-row, 64-key) tile of the mask (17 x 97 of them),
+    # padded to 256 bytes, then one 64-bit word per mask row and 64-key tile
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == \
-        2560 + 6152 * 97 * 8
+        1792 + 6152 * 97 * 8
     assert b.sp_masked_attention_workspace_size(1, 2, 300, 128, 4, 64, b.SP_BF16, True, 300 * 128) == \
         256 + 2 * 300 * 2 * 8
     # Without a mask the workspace holds the partial records of split launches:
-    # one rank's share of the 6144-token video workload (96 query tiles of 48
+    # one rank's share of the 6144-token video workload (64 query tiles of 48
     # key tiles) splits over the 256 CUs (assumed when no GPU can be queried):
-    # two records of 256 rows x (128 + 2) floats per workgroup.
+    # two records of 384 rows x (128 + 2) floats per workgroup.
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == \
-        2 * 256 * 256 * 130 * 4
+        2 * 256 * 384 * 130 * 4
     # all eight shares fill the GPU; the cross share's 8 key tiles are too few
     # to pay for the merge; the fp32 kernel never splits
     assert b.sp_masked_attention_workspace_size(8, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == 0

@@ -1,8 +1,8 @@
 """GPU parity of sp_masked_attention against the float64 CPU oracle.
 
 Tolerance (max-abs vs the oracle on the same input bytes): 2e-2 for bf16 and
-1e-4 for fp32.  Shapes span several 128-row query tiles and 64-key tiles with
-ragged tails; masks exercise the empty / full / partial tile classes, the
+1e-4 for fp32.  Shapes span several query tiles (384 rows for bf16, 128 for
+fp32) and 128-key tiles with ragged tails; masks exercise the empty / full / partial tile classes, the
 key-only padding mask and rows with nothing visible."""
 
 import math
@@ -46,6 +46,8 @@ def run_case(dtype, D, R, B, Tq, Tk, Hl, kv_valid, mask=None, seed=0, scale=None
 CASES = [
     # dtype, D, R, B, Tq, Tk, Hl, kv_valid, mask kind
     ("bf16", 128, 2, 1, 300, 333, 2, 333, None),
+    ("bf16", 128, 1, 1, 1000, 333, 2, 333, None),       # three query tiles, the last ragged
+    ("bf16", 64, 1, 2, 800, 260, 2, 255, None),
     ("bf16", 128, 1, 2, 128, 64, 1, 64, None),          # exactly one tile each way
     ("bf16", 128, 2, 2, 257, 200, 3, 150, None),        # key-only padding inside a tile
     ("bf16", 64, 2, 1, 390, 1024, 4, 987, None),        # the cross workload's key padding
@@ -53,6 +55,8 @@ CASES = [
     ("bf16", 128, 1, 1, 300, 300, 2, 300, "random"),
     ("bf16", 128, 2, 2, 260, 260, 2, 258, "blocks"),    # empty/full/partial tiles + padding
     ("bf16", 64, 1, 3, 200, 190, 2, 190, "blocks_b"),   # per-batch masks
+    ("bf16", 128, 1, 1, 1000, 700, 2, 690, "blocks"),   # class rows of three query tiles
+    ("bf16", 64, 1, 2, 800, 400, 1, 400, "random"),
     ("f32", 16, 4, 1, 52, 52, 2, 50, None),             # the tiny workload's rank share
     ("f32", 64, 1, 2, 200, 150, 2, 133, None),
     ("f32", 128, 1, 1, 140, 130, 2, 130, "random"),
