@@ -97,7 +97,8 @@ struct AttnArgs {
   const uint8_t* mask;                   // (B, Tq, Tk) or null
   int64_t mask_bs;                       // batch stride of mask (0 = shared)
   const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt), BM x BN tiles
-  const uint64_t* bits;                  // visibility words (Bm, nkt, Tq): bit j = key BN*kt + j
+  const uint64_t* bits;                  // visibility words (Bm, nkt, ldw): bit j = key BN*kt + j
+  int64_t ldw;                           // rows per class tile of bits: Tq rounded up to even
   int32_t nqt, nkt;                      // query tiles of this kernel, key tiles of BN
   int32_t nqt_cls;                       // query tiles of the class map (height BM)
   float c;                               // scale * log2(e)
@@ -215,6 +216,10 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // from LDS, so that looking up a tile's class never waits on global memory
   // (a wait for a global load would also wait for the K/V tile in flight)
   __shared__ uint8_t cls_lds[MASK ? kMaxClassTiles : 4];
+  // visibility words of the key tiles in flight (partial tiles only): buffer i
+  // holds, for each BN-key class tile c of its key tile, the words of this
+  // workgroup's BM rows at [c * BM + row]; filled by direct loads with K/V
+  __shared__ __attribute__((aligned(16))) uint64_t mw_lds[MASK ? NBUF * (KT / BN) * BM : 2];
   auto kbuf = [&](auto i) __attribute__((always_inline)) -> char* {
     constexpr int I = decltype(i)::value;
     return I == 0 ? k_lds0 : (I == 1 ? k_lds1 : k_lds2);
@@ -286,12 +291,11 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   }
 
   const uint8_t* cls_row = nullptr;
-  const uint64_t* brow[QB] = {};
+  const uint64_t* wbase = nullptr;   // visibility words of this batch's mask, class tile 0
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) brow[qb] = a.bits + bm * a.nkt * a.Tq + (qvalid[qb] ? qrow[qb] : 0);
+    wbase = a.bits + bm * a.nkt * a.ldw;
     for (int i = tid; i < a.nkt; i += BF16_THREADS) cls_lds[i] = cls_row[i];
     __syncthreads();
   }
@@ -329,15 +333,22 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // checked by the descriptor).  The FLAT-encoded global_load_lds would do
   // the same copy, but while one of those is in flight the compiler cannot
   // count LDS reads precisely and waits for all of them before every MFMA.
-  const int ld_c = lane / KPG;
-  const int ld_n = (KPG == 8 ? ((lane % KPG) ^ (4 * (ld_c & 1))) : (lane % KPG));
+  //
+  // The lane offsets are recomputed from the lane index at every issue (a few
+  // VALU ops per tile): kept live across the tile loop they are the first
+  // values the register allocator spills at three waves per SIMD, and a
+  // reload before each load then waits for every load in flight.
   const int wu = __builtin_amdgcn_readfirstlane(w);          // wave index, as a scalar
   const int32_t kst = int32_t(a.ks[2]) * 2, vst = int32_t(a.vs[2]) * 2;   // token strides in bytes (host-checked)
-  const int32_t k_lane = ld_n * kst + 16 * ld_c;
-  const int32_t v_lane = ld_n * vst + 16 * ld_c;
   const int32_t k_nrec = (KT - 1) * kst + 2 * D, v_nrec = (KT - 1) * vst + 2 * D;
   constexpr int32_t kRsrcWord3 = 0x00020000;   // raw 32-bit data format, no swizzle
   auto issue = [&](int kt, char* kdst, char* vdst) __attribute__((always_inline)) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));   // opaque: not hoisted out of the tile loop
+    const int ld_c = ln / KPG;
+    const int ld_n = (KPG == 8 ? ((ln % KPG) ^ (4 * (ld_c & 1))) : (ln % KPG));
+    const int32_t k_lane = ld_n * kst + 16 * ld_c;
+    const int32_t v_lane = ld_n * vst + 16 * ld_c;
     const int64_t key0 = int64_t(kt) * KT;
     const __amdgpu_buffer_rsrc_t krs =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(kp + key0 * a.ks[2]), 0, k_nrec, kRsrcWord3);
@@ -379,21 +390,27 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // QK^T MFMAs of part k+1 while computing the exponentials of part k, so the
   // MFMA unit has independent work while the VALU runs the softmax; the rare
   // rescale branch comes after.
-  // Visibility words of this lane's rows for the BN-key class tiles of tile
-  // kt (partial tiles only).  They are loaded one tile ahead, right after that
-  // tile's K/V loads, and so have arrived by the wait for those.
-  using MaskWords = uint64_t[QB][KT / BN];
-  auto load_words = [&](int kt, MaskWords& mw) __attribute__((always_inline)) {
-    if (!MASK || kt >= nkt_eff || tile_class(kt) != kTilePartial) return;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
-#pragma unroll
-      for (int c = 0; c < KT / BN; ++c) {
-        const int ct = kt * (KT / BN) + c;
-        mw[qb][c] = (qvalid[qb] && ct < a.nkt) ? brow[qb][int64_t(ct) * a.Tq] : 0ull;
-      }
+  // Visibility words of the workgroup's rows for the BN-key class tiles of a
+  // partial tile kt: one 16-byte direct load per wave for the first WLOADS
+  // waves (two rows per lane), issued with that tile's K/V loads into the same
+  // pipeline stage, so the same wait and barrier cover them.  The rows of a
+  // class tile are ldw (even) words apart, so every 16-byte unit holds two
+  // rows of one class tile; the descriptor ends at the tile's last class
+  // tile, and rows past Tq (never stored) read another tile's words or zero.
+  constexpr int WROWS = 2 * 64;                       // rows per wave-wide load
+  constexpr int WLOADS = (KT / BN) * (BM / WROWS);
+  static_assert(BM % WROWS == 0 && WLOADS <= BF16_WAVES, "one word load per wave");
+  auto issue_words = [&](int kt, uint64_t* dst) __attribute__((always_inline)) {
+    if (!MASK || kt >= nkt_eff || wu >= WLOADS || tile_class(kt) != kTilePartial) return;
+    const int c = wu / (BM / WROWS), r0 = (wu % (BM / WROWS)) * WROWS;
+    const int ncls = a.nkt - kt * (KT / BN) < KT / BN ? a.nkt - kt * (KT / BN) : KT / BN;
+    if (c >= ncls) return;
+    const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint64_t*>(wbase + int64_t(kt) * (KT / BN) * a.ldw), 0, int32_t(ncls * a.ldw * 8), kRsrcWord3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + c * BM + r0), 16, 16 * lane,
+                                             int32_t((c * a.ldw + int64_t(tc.qt) * BM + r0) * 8), 0, 0);
   };
-  auto compute = [&](int kt, const char* kb_, const char* vb_, const MaskWords& mw) __attribute__((always_inline)) {
+  auto compute = [&](int kt, const char* kb_, const char* vb_, const uint64_t* mwl) __attribute__((always_inline)) {
     constexpr int NP = KT / 32;   // parts per tile
     const int64_t key0 = int64_t(kt) * KT;
     const uint8_t cls = tile_class(kt);
@@ -485,7 +502,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 #pragma unroll
         for (int qb = 0; qb < QB; ++qb) {
           // bit 8*(v/4) + v%4 of wsh is register v's key
-          const uint32_t wsh = MASK ? uint32_t(mw[qb][kb / 2] >> (32 * (kb & 1) + 4 * h)) : 0u;
+          const uint32_t wsh =
+              MASK ? uint32_t(mwl[(kb / 2) * BM + 32 * QB * w + 32 * qb + l32] >> (32 * (kb & 1) + 4 * h)) : 0u;
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
             const int kofs = 8 * (v >> 2) + (v & 3);
@@ -542,11 +560,12 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   ahead[0] = MASK ? next_tile(kt_first - 1) : kt_first;
 #pragma unroll
   for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff);
-  MaskWords mwb[NBUF] = {};   // stage S computes with mwb[S]
+  constexpr int MWB = (KT / BN) * BM;   // words per mask-word buffer
   if (ahead[0] < nkt_eff) issue(ahead[0], kbuf(I0{}), vbuf(I0{}));
-  load_words(ahead[0], mwb[0]);
+  issue_words(ahead[0], mw_lds);
   if constexpr (NBUF > 2) {
     if (ahead[1] < nkt_eff) issue(ahead[1], kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
+    issue_words(ahead[1], mw_lds + MWB);
   }
   auto stage = [&](auto sidx) __attribute__((always_inline)) -> bool {
     constexpr int S = decltype(sidx)::value;
@@ -564,8 +583,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     ahead[NBUF - 1] = next_tile(ahead[NBUF - 2] < nkt_eff ? ahead[NBUF - 2] : nkt_eff);
     using NX = std::integral_constant<int, (S + NBUF - 1) % NBUF>;
     if (ahead[NBUF - 2] < nkt_eff) issue(ahead[NBUF - 2], kbuf(NX{}), vbuf(NX{}));
-    load_words(ahead[0], mwb[(S + 1) % NBUF]);
-    compute(kt, kbuf(sidx), vbuf(sidx), mwb[S]);
+    issue_words(ahead[NBUF - 2], mw_lds + NX::value * MWB);
+    compute(kt, kbuf(sidx), vbuf(sidx), mw_lds + S * MWB);
     return true;
   };
   for (;;) {
@@ -825,7 +844,7 @@ __device__ __forceinline__ uint64_t nonzero_bytes_to_bits(uint64_t x) {
 
 __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
                                                                int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
-                                                               uint64_t* bits) {
+                                                               uint64_t* bits, int64_t ldw) {
   static_assert(BN == 64, "one 64-bit word per row and tile");
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
@@ -847,7 +866,7 @@ __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* 
     } else {
       for (int c = 0; c < n; ++c) word |= uint64_t(p[c] != 0) << c;
     }
-    bits[(b * nkt + kt) * Tq + row] = word;   // rows contiguous per class tile
+    bits[(b * nkt + kt) * ldw + row] = word;   // rows contiguous per class tile
     any |= word != 0;
     all &= word == full;
   }
@@ -949,9 +968,9 @@ int64_t mask_ws_bytes(int64_t B, int64_t Tq, int64_t Tk, bool has_mask, int64_t 
   if (!has_mask) return 0;
   const int64_t bm = mask_batch_stride ? B : 1;
   // one class byte per BM x BN tile, then (256-byte aligned) one 64-bit
-  // visibility word per mask row and BN-key tile
+  // visibility word per mask row (Tq rounded up to even) and BN-key tile
   const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
-  return cls_bytes + bm * Tq * div_up(Tk, BN) * 8;
+  return cls_bytes + bm * div_up(Tq, 2) * 2 * div_up(Tk, BN) * 8;
 }
 
 extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
@@ -1007,6 +1026,8 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride);
   if (has_mask && (workspace == nullptr || workspace_bytes < size_t(mask_bytes))) return SP_ERR_INVALID_ARG;
   if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
+  // (grid limits; nqt_cls also keeps the visibility-word offsets, below
+  // 2 * 8 * ldw bytes, inside 32 bits)
   if (has_mask && (B > 65535 || nqt_cls > 65535)) return SP_ERR_UNSUPPORTED;
 
   AttnArgs a;
@@ -1025,6 +1046,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
     const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
     a.bits = reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + cls_bytes);
   }
+  a.ldw = div_up(Tq, 2) * 2;
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
   a.c = scale * 1.4426950408889634f;
   a.nwg = uint32_t(nwg);
@@ -1048,7 +1070,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
     const int64_t bm = mask_batch_stride ? B : 1;
     hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt_cls), unsigned(bm)), dim3(kThreads), 0,
                        s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
-                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits));
+                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw);
     if (launch_status() != SP_OK) return SP_ERR_HIP;
     return dispatch_d<true>(D, a, dtype, s);
   }

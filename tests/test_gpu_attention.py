@@ -57,6 +57,7 @@ CASES = [
     ("bf16", 64, 1, 3, 200, 190, 2, 190, "blocks_b"),   # per-batch masks
     ("bf16", 128, 1, 1, 1000, 700, 2, 690, "blocks"),   # class rows of three query tiles
     ("bf16", 64, 1, 2, 800, 400, 1, 400, "random"),
+    ("bf16", 128, 1, 1, 777, 430, 2, 425, "random"),    # odd Tq, odd count of 64-key class tiles
     ("f32", 16, 4, 1, 52, 52, 2, 50, None),             # the tiny workload's rank share
     ("f32", 64, 1, 2, 200, 150, 2, 133, None),
     ("f32", 128, 1, 1, 140, 130, 2, 130, "random"),
@@ -104,6 +105,7 @@ SPLIT_CASES = [
     (128, 1, 1, 600, 2000, 2, 2000, "blocks"),   # staircase mask: empty, full and partial segments
     (128, 1, 2, 520, 1800, 2, 1800, "blocks_b"),  # per-batch masks
     (64, 1, 1, 300, 2100, 3, 2100, "random"),    # a row with no visible key stays 0
+    (128, 1, 1, 599, 1990, 2, 1985, "blocks"),   # odd Tq and class-tile count
 ]
 
 
