@@ -35,8 +35,8 @@
 //     between rescales; row sums add the bf16-rounded p with v_dot2;
 //   * user masks are classified once per call into empty/full/partial tiles:
 //     empty tiles are skipped, full tiles read no mask bytes, partial tiles one
-//     64-bit visibility word per row and 64 keys (loaded a tile ahead; the
-//     tile classes of a query tile's row sit in LDS);
+//     64-bit visibility word per row and 64 keys (direct loads into LDS with
+//     the tile's K/V; the tile classes of a query tile's row sit in LDS too);
 //   * without a user mask, workgroup ids are remapped so that the 8 XCDs each
 //     take a contiguous run of (rank, batch, head) groups: the q-tiles sharing
 //     one head's K/V run on the same XCD and share its L2; with a user mask
@@ -55,11 +55,11 @@ namespace {
 
 constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
 // Waves per bf16 workgroup: 12, three per SIMD (measured +4-6 % over 8).  At
-// three waves the D = 128 kernels sit at the 168-VGPR limit and the compiler
-// spills a few 64-bit values of the edge-tile load path to scratch (reloaded
-// once per query tile, outside the per-part work); after any change, check
-// that no scratch access lands in the per-tile path (the tile loop's load
-// issue and compute blocks), which costs 5-10 %.
+// three waves the D = 128 kernels sit at the 168-VGPR limit; the plain kernel
+// has no scratch access and the others a few reloads outside the per-part
+// work.  After any change, check that no scratch access lands in the
+// per-tile path (the tile loop's load issue and compute blocks): a reload
+// there waits for every load in flight and costs 5-12 %.
 constexpr int BF16_WAVES = 12;
 constexpr int BF16_THREADS = 64 * BF16_WAVES;
 constexpr int BM = 32 * QB * BF16_WAVES;   // query rows per bf16 workgroup, and the mask-class tile height
