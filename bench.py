@@ -36,15 +36,23 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def code_text(src: str) -> str:
+    """C++ source without comments and with whitespace runs collapsed: what
+    the compiler sees, so that a comment edit does not change the hash."""
+    src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+    src = re.sub(r"//[^\n]*", " ", src)
+    return " ".join(src.split())
+
+
 def kernel_hash(*names) -> str:
-    """Hash of the named kernel sources and of the compiler flags they are
-    built with (build.py), so that a profile taken on other code or flags is
-    never reported as current."""
+    """Hash of the named kernel sources (their code, not their comments) and
+    of the compiler flags they are built with (build.py), so that a profile
+    taken on other code or flags is never reported as current."""
     from sequence_attention_video_amd import build as b
     h = hashlib.sha256()
     for n in names:
-        with open(os.path.join(ROOT, "sequence_attention_video_amd", "csrc", n), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, "sequence_attention_video_amd", "csrc", n), encoding="utf-8") as f:
+            h.update(code_text(f.read()).encode())
         flags = [f for f in b.compile_flags() + b.EXTRA_FLAGS.get(n, []) if not os.path.isabs(f)]
         h.update(" ".join(flags).encode())
     return h.hexdigest()[:16]
