@@ -339,6 +339,9 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // values the register allocator spills at three waves per SIMD, and a
   // reload before each load then waits for every load in flight.
   const int wu = __builtin_amdgcn_readfirstlane(w);          // wave index, as a scalar
+  // Waves whose query rows all lie past Tq (in the last query tile of a
+  // ragged Tq) still share the loads and barriers but skip the compute.
+  const bool wave_has_rows = int64_t(tc.qt) * BM + 32 * QB * wu < a.Tq;
   const int32_t kst = int32_t(a.ks[2]) * 2, vst = int32_t(a.vs[2]) * 2;   // token strides in bytes (host-checked)
   const int32_t k_nrec = (KT - 1) * kst + 2 * D, v_nrec = (KT - 1) * vst + 2 * D;
   constexpr int32_t kRsrcWord3 = 0x00020000;   // raw 32-bit data format, no swizzle
@@ -584,7 +587,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     using NX = std::integral_constant<int, (S + NBUF - 1) % NBUF>;
     if (ahead[NBUF - 2] < nkt_eff) issue(ahead[NBUF - 2], kbuf(NX{}), vbuf(NX{}));
     issue_words(ahead[NBUF - 2], mw_lds + NX::value * MWB);
-    compute(kt, kbuf(sidx), vbuf(sidx), mw_lds + S * MWB);
+    if (wave_has_rows) compute(kt, kbuf(sidx), vbuf(sidx), mw_lds + S * MWB);
     return true;
   };
   for (;;) {
