@@ -54,20 +54,31 @@ namespace sp {
 namespace {
 
 constexpr int QB = 1;                // 32-row query blocks per wave of the bf16 kernel
-// Waves per bf16 workgroup: 12, three per SIMD (measured +4-6 % over 8).  At
-// three waves the D = 128 kernels sit at the 168-VGPR limit; the plain kernel
-// has no scratch access and the others a few reloads outside the per-part
-// work.  After any change, check that no scratch access lands in the
-// per-tile path (the tile loop's load issue and compute blocks): a reload
-// there waits for every load in flight and costs 5-12 %.
-constexpr int BF16_WAVES = 12;
-constexpr int BF16_THREADS = 64 * BF16_WAVES;
-constexpr int BM = 32 * QB * BF16_WAVES;   // query rows per bf16 workgroup, and the mask-class tile height
+// Waves per bf16 workgroup, by head dim.  D = 128: 12 waves, three per SIMD,
+// one workgroup per CU (its K/V buffers take 136 KiB of LDS; measured +4-6 %
+// over 8 waves).  D = 64: 8 waves, and the buffers take 68 KiB, so two
+// workgroups share a CU at four waves per SIMD (128 VGPRs): one workgroup's
+// prologue and epilogue overlap the other's tiles (measured +3 % on long key
+// ranges, +10-20 % on the 1024-key cross-attention launches).  At three waves
+// the D = 128 kernels sit at the 168-VGPR limit; the plain kernel has no
+// scratch access and the others a few reloads outside the per-part work.
+// After any change, check that no scratch access lands in the per-tile path
+// (the tile loop's load issue and compute blocks): a reload there waits for
+// every load in flight and costs 5-12 %.
+template <int D>
+constexpr int kWaves = D == 64 ? 8 : 12;
+template <int D>
+constexpr int kWavesPerSimd = D == 64 ? 4 : 3;
+// query rows per bf16 workgroup, and the height of the mask-class tiles of
+// bf16 launches
+template <int D>
+constexpr int kRows = 32 * QB * kWaves<D>;
 constexpr int BM32 = 128;            // query rows per fp32 workgroup
+constexpr int kClsRowsF32 = 384;     // mask-class tile height of fp32 launches (a multiple of BM32)
 constexpr int BN = 64;               // keys per tile (all kernels, and the mask-class tile width)
 constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a multiple of BN)
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
-static_assert(BM % BM32 == 0, "an fp32 query tile lies inside one class tile");
+static_assert(kClsRowsF32 % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
 constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
@@ -96,11 +107,11 @@ struct AttnArgs {
   int64_t kv_end;                        // keys >= kv_end are never visible
   const uint8_t* mask;                   // (B, Tq, Tk) or null
   int64_t mask_bs;                       // batch stride of mask (0 = shared)
-  const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt), BM x BN tiles
+  const uint8_t* cls;                    // tile classes (Bm, nqt_cls, nkt) of class-tile rows x BN keys
   const uint64_t* bits;                  // visibility words (Bm, nkt, ldw): bit j = key BN*kt + j
   int64_t ldw;                           // rows per class tile of bits: Tq rounded up to even
   int32_t nqt, nkt;                      // query tiles of this kernel, key tiles of BN
-  int32_t nqt_cls;                       // query tiles of the class map (height BM)
+  int32_t nqt_cls;                       // query tiles of the class map
   float c;                               // scale * log2(e)
   uint32_t nwg;
   // split launches (bf16, no user mask): the key tiles of all items in order
@@ -175,7 +186,7 @@ template <int D>
 struct Bf16Tile {
   static constexpr int KPG = 512 / D;               // keys per 1 KiB group
   static constexpr int NG = KT / KPG;               // groups per tile = direct loads per tile
-  static constexpr int NLD = (NG + BF16_WAVES - 1) / BF16_WAVES;   // direct loads per wave per tile and tensor (at most)
+  static constexpr int NLD = (NG + kWaves<D> - 1) / kWaves<D>;   // direct loads per wave per tile and tensor (at most)
   static constexpr int GROUP_BYTES = 1024 + 64;
   static constexpr int TILE_BYTES = NG * GROUP_BYTES;
   static constexpr int NKS = D / 16;                // k-steps of QK^T
@@ -200,7 +211,9 @@ __device__ __forceinline__ void wait_vmem() {
 }
 
 template <int D, bool MASK, bool SPLIT>
-__global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * kWaves<D>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
+void attn_bf16_kernel(AttnArgs a) {
+  constexpr int WAVES = kWaves<D>, THREADS = 64 * WAVES, BM = kRows<D>;
   using T = Bf16Tile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD, NG = T::NG;
   constexpr int LOADS = 2 * NLD;   // direct loads per wave per tile (K and V)
@@ -296,7 +309,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
     wbase = a.bits + bm * a.nkt * a.ldw;
-    for (int i = tid; i < a.nkt; i += BF16_THREADS) cls_lds[i] = cls_row[i];
+    for (int i = tid; i < a.nkt; i += THREADS) cls_lds[i] = cls_row[i];
     __syncthreads();
   }
   // Key tiles of KT keys; with a user mask a tile's class combines the classes
@@ -360,8 +373,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     if (key0 + KT <= a.kv_end) {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int grp = j * BF16_WAVES + wu;
-        if (NG % BF16_WAVES != 0 && grp >= NG) break;
+        const int grp = j * WAVES + wu;
+        if (NG % WAVES != 0 && grp >= NG) break;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16, k_lane,
                                                  grp * KPG * kst, 0, 0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(vrs, (lds_void*)(vdst + grp * T::GROUP_BYTES), 16, v_lane,
@@ -370,8 +383,8 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
     } else {
 #pragma unroll
       for (int j = 0; j < NLD; ++j) {
-        const int grp = j * BF16_WAVES + wu;
-        if (NG % BF16_WAVES != 0 && grp >= NG) break;
+        const int grp = j * WAVES + wu;
+        if (NG % WAVES != 0 && grp >= NG) break;
         int32_t n = grp * KPG + ld_n;                       // key - key0
         if (key0 + n >= a.kv_end) n = int32_t(a.kv_end - 1 - key0);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(krs, (lds_void*)(kdst + grp * T::GROUP_BYTES), 16,
@@ -402,7 +415,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
   // tile, and rows past Tq (never stored) read another tile's words or zero.
   constexpr int WROWS = 2 * 64;                       // rows per wave-wide load
   constexpr int WLOADS = (KT / BN) * (BM / WROWS);
-  static_assert(BM % WROWS == 0 && WLOADS <= BF16_WAVES, "one word load per wave");
+  static_assert(BM % WROWS == 0 && WLOADS <= WAVES, "one word load per wave");
   auto issue_words = [&](int kt, uint64_t* dst) __attribute__((always_inline)) {
     if (!MASK || kt >= nkt_eff || wu >= WLOADS || tile_class(kt) != kTilePartial) return;
     const int c = wu / (BM / WROWS), r0 = (wu % (BM / WROWS)) * WROWS;
@@ -647,6 +660,7 @@ __global__ __launch_bounds__(BF16_THREADS) void attn_bf16_kernel(AttnArgs a) {
 // visible.  One workgroup per (item, 64 rows); 4 threads per row.
 template <int D, bool MASK>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
+  constexpr int BM = kRows<D>;
   constexpr int DPT = D / 4;   // dims per thread
   const uint32_t item = blockIdx.x;
   const int row = blockIdx.y * 64 + (threadIdx.x >> 2);
@@ -724,8 +738,8 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const uint8_t* mrow = nullptr;
   if (MASK) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
-    // a class tile is BM rows high: it holds this workgroup's BM32 rows
-    cls_row = a.cls + (bm * a.nqt_cls + tc.qt * BM32 / BM) * int64_t(a.nkt);
+    // a class tile is kClsRowsF32 rows high: it holds this workgroup's BM32 rows
+    cls_row = a.cls + (bm * a.nqt_cls + tc.qt * BM32 / kClsRowsF32) * int64_t(a.nkt);
     mrow = a.mask + tc.b * a.mask_bs + qrow * a.Tk;
   }
 
@@ -847,7 +861,7 @@ __device__ __forceinline__ uint64_t nonzero_bytes_to_bits(uint64_t x) {
 
 __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
                                                                int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
-                                                               uint64_t* bits, int64_t ldw) {
+                                                               uint64_t* bits, int64_t ldw, int32_t rows) {
   static_assert(BN == 64, "one 64-bit word per row and tile");
   const int kt = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
@@ -855,8 +869,8 @@ __global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* 
   const int n = int(Tk - col0 < BN ? Tk - col0 : BN);           // in-range keys of the tile
   const uint64_t full = n == 64 ? ~0ull : ((1ull << n) - 1);
   int any = 0, all = 1;
-  for (int r = threadIdx.x; r < BM; r += kThreads) {
-    const int64_t row = int64_t(qt) * BM + r;
+  for (int r = threadIdx.x; r < rows; r += kThreads) {
+    const int64_t row = int64_t(qt) * rows + r;
     if (row >= Tq) break;
     const uint8_t* p = mask + b * mask_bs + row * Tk + col0;
     uint64_t word = 0;
@@ -903,10 +917,10 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
     if constexpr (D % 32 == 0) {
       if (a.part) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
-                           dim3(BF16_THREADS), 0, s, a);
-        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, BM / 64), dim3(kThreads), 0, s, a);
+                           dim3(64 * kWaves<D>), 0, s, a);
+        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, kRows<D> / 64), dim3(kThreads), 0, s, a);
       } else {
-        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(BF16_THREADS), 0, s, a);
+        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(64 * kWaves<D>), 0, s, a);
       }
     }
   } else {
@@ -962,18 +976,29 @@ int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D) {
   return plain * 10 >= (upw + fixed) * 13 ? upw : 0;
 }
 
-// bytes of partial records of a split launch: two slots per workgroup
-int64_t split_bytes(int64_t ncu, int32_t D) { return 2 * ncu * BM * (int64_t(D) + 2) * 4; }
+// query rows per workgroup of the bf16 kernel for head dim D (64 or 128)
+int64_t bf16_rows(int32_t D) { return D == 64 ? kRows<64> : kRows<128>; }
 
-// Bytes of the mask part of the workspace (class bytes, then 256-byte aligned
-// visibility words); 0 without a mask.
-int64_t mask_ws_bytes(int64_t B, int64_t Tq, int64_t Tk, bool has_mask, int64_t mask_batch_stride) {
+// height of the mask-class tiles of a launch: the bf16 kernel's query tile,
+// or kClsRowsF32 for the fp32 kernel
+int64_t cls_rows(sp_dtype dtype, int32_t D) { return dtype == SP_BF16 ? bf16_rows(D) : kClsRowsF32; }
+
+// bytes of partial records of a split launch: two slots per workgroup
+int64_t split_bytes(int64_t ncu, int32_t D) { return 2 * ncu * bf16_rows(D) * (int64_t(D) + 2) * 4; }
+
+// bytes of the class part of the workspace: one class byte per (class tile
+// rows x BN) tile, padded to 256 bytes
+int64_t cls_ws_bytes(int64_t bm, int64_t Tq, int64_t Tk, int64_t rows) {
+  return (bm * div_up(Tq, rows) * div_up(Tk, BN) + 255) / 256 * 256;
+}
+
+// Bytes of the mask part of the workspace (class bytes, then one 64-bit
+// visibility word per mask row (Tq rounded up to even) and BN-key tile); 0
+// without a mask.
+int64_t mask_ws_bytes(int64_t B, int64_t Tq, int64_t Tk, bool has_mask, int64_t mask_batch_stride, int64_t rows) {
   if (!has_mask) return 0;
   const int64_t bm = mask_batch_stride ? B : 1;
-  // one class byte per BM x BN tile, then (256-byte aligned) one 64-bit
-  // visibility word per mask row (Tq rounded up to even) and BN-key tile
-  const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
-  return cls_bytes + bm * div_up(Tq, 2) * 2 * div_up(Tk, BN) * 8;
+  return cls_ws_bytes(bm, Tq, Tk, rows) + bm * div_up(Tq, 2) * 2 * div_up(Tk, BN) * 8;
 }
 
 extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
@@ -983,11 +1008,11 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   // [mask classes and words][partial records of a split launch, 256-byte
   // aligned]; the split part is sized for kv_valid_len = Tk (a shorter key
   // range needs no more)
-  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask != 0, mask_batch_stride);
+  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask != 0, mask_batch_stride, cls_rows(dtype, D));
   int64_t split = 0;
   if (dtype == SP_BF16 && (D == 64 || D == 128)) {
     const int64_t ncu = device_cus();
-    const int64_t items = div_up(Tq, BM) * Hl * B * R;
+    const int64_t items = div_up(Tq, bf16_rows(D)) * Hl * B * R;
     if (split_units_per_wg(items, div_up(Tk, KT), ncu, D)) split = split_bytes(ncu, D);
   }
   return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
@@ -1017,8 +1042,9 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (overlap(o, on, q, span_bytes(qs, R, B, Tq, Hl, D, eb)) || overlap(o, on, k, span_bytes(ks, R, B, tk1, Hl, D, eb)) ||
       overlap(o, on, v, span_bytes(vs, R, B, tk1, Hl, D, eb)))
     return SP_ERR_INVALID_ARG;
-  const int64_t nqt = div_up(Tq, dtype == SP_BF16 ? BM : BM32), nkt = div_up(Tk, BN);
-  const int64_t nqt_cls = div_up(Tq, BM);
+  const int64_t crows = cls_rows(dtype, D);
+  const int64_t nqt = div_up(Tq, dtype == SP_BF16 ? bf16_rows(D) : BM32), nkt = div_up(Tk, BN);
+  const int64_t nqt_cls = div_up(Tq, crows);
   const int64_t nwg = nqt * Hl * B * R;
   if (nwg >= (int64_t(1) << 31) || nkt >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
   // the bf16 kernel addresses one key tile of K and of V with 32-bit byte offsets
@@ -1026,7 +1052,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
     return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
   if (dtype == SP_BF16 && has_mask && nkt > kMaxClassTiles) return SP_ERR_UNSUPPORTED;
-  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride);
+  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride, crows);
   if (has_mask && (workspace == nullptr || workspace_bytes < size_t(mask_bytes))) return SP_ERR_INVALID_ARG;
   if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
   // (grid limits; nqt_cls also keeps the visibility-word offsets, below
@@ -1046,8 +1072,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   a.cls = static_cast<const uint8_t*>(workspace);
   {
     const int64_t bm = mask_batch_stride ? B : 1;
-    const int64_t cls_bytes = (bm * div_up(Tq, BM) * div_up(Tk, BN) + 255) / 256 * 256;
-    a.bits = reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + cls_bytes);
+    a.bits = reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + cls_ws_bytes(bm, Tq, Tk, crows));
   }
   a.ldw = div_up(Tq, 2) * 2;
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
@@ -1073,7 +1098,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
     const int64_t bm = mask_batch_stride ? B : 1;
     hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt_cls), unsigned(bm)), dim3(kThreads), 0,
                        s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
-                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw);
+                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw, int32_t(crows));
     if (launch_status() != SP_OK) return SP_ERR_HIP;
     return dispatch_d<true>(D, a, dtype, s);
   }
