@@ -8,8 +8,9 @@
 // keys visible).
 //
 // Design (bf16):
-//   * one workgroup = 12 waves = 384 query rows of one (rank, batch, head);
-//     each wave owns 32 query rows for the whole key loop, and three waves
+//   * one workgroup = 12 waves = 384 query rows of one (rank, batch, head)
+//     at D = 128 (8 waves = 256 rows at D = 64, two workgroups per CU); each
+//     wave owns 32 query rows for the whole key loop, and three (four) waves
 //     share each SIMD, so one wave's softmax (VALU) runs while another's MFMAs
 //     do.  The kernel is templated on query blocks per wave (QB); two blocks
 //     per wave would let every LDS operand feed two MFMAs, but at D = 128 the
@@ -90,7 +91,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -114,7 +114,7 @@ struct AttnArgs {
   int32_t nqt_cls;                       // query tiles of the class map
   float c;                               // scale * log2(e)
   uint32_t nwg;
-  // split launches (bf16, no user mask): the key tiles of all items in order
+  // split launches (bf16): the key tiles of all items in order
   int64_t units;                         // items * nku
   int64_t upw;                           // units per workgroup (< nku)
   int32_t nku;                           // key tiles of KT per item
