@@ -247,12 +247,13 @@ void attn_bf16_kernel(AttnArgs a) {
   const int l32 = lane & 31, h = lane >> 5;
 
   // Work split.  Without SPLIT a workgroup runs one item over all of its key
-  // tiles.  With SPLIT (launches whose items cannot fill the GPU) the key
-  // tiles of all items, item after item, form one sequence of units, and
-  // logical workgroup g runs units [g*upw, (g+1)*upw).  As upw < nku that is at
-  // most two segments of at most two items; each segment ends in a partial
-  // record (unnormalised O rows, running max and sum) in slot 2*g + segment,
-  // which attn_combine_kernel merges into O.
+  // tiles.  With SPLIT (launches whose items do not divide evenly over the
+  // GPU) the key tiles of all items, item after item, form one sequence of
+  // units, and logical workgroup g runs units [g*upw, (g+1)*upw): one segment
+  // per item it meets.  A segment that covers a whole item ends like an
+  // unsplit one; only the first and the last segment of a range can be
+  // partial, and each of those ends in a partial record (unnormalised O rows,
+  // running max and sum) that attn_combine_kernel merges into O.
   const uint32_t gl = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0u;
   int64_t u_next = SPLIT ? int64_t(gl) * a.upw : 0;
   const int64_t u_end = SPLIT ? (a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
@@ -611,14 +612,18 @@ void attn_bf16_kernel(AttnArgs a) {
     }
   }
 
-  // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4
+  // O^T accumulator: lane (l32, h), register v of block d is dim 32*d + 8*(v/4) + 4*h + v%4.
+  // A segment that covers its whole item writes O; a partial one (split
+  // launches) writes a record, in slot 2*g if it is the workgroup's first
+  // segment, else (it is then the last) in slot 2*g + 1.
+  const bool direct = !SPLIT || (kt_first == 0 && kt_stop == a.nku);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
-    if constexpr (SPLIT) {
+    if (!direct) {
       // partial record: O rows (fp32, unnormalised), then m and l per row
       const int row = 32 * QB * w + 32 * qb + l32;
-      float* rec = a.part + int64_t(2 * gl + seg) * (BM * (D + 2));
+      float* rec = a.part + int64_t(2 * gl + (seg > 0 ? 1 : 0)) * (BM * (D + 2));
       if (qvalid[qb]) {
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
@@ -668,9 +673,11 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const TileCoord tc = decode_item<MASK>(a, item);
   const int64_t qrow = int64_t(tc.qt) * BM + row;
   if (qrow >= a.Tq) return;
-  // workgroups whose unit ranges meet this item, and the slot of each
+  // workgroups whose unit ranges meet this item, and the slot of each; an
+  // item inside one range was written whole by its workgroup
   const int64_t u0 = int64_t(item) * a.nku, u1 = u0 + a.nku;   // this item's units
   const int64_t g_first = u0 / a.upw, g_last = (u1 - 1) / a.upw;
+  if (g_first == g_last) return;
   float mx = -INFINITY;
   for (int64_t g = g_first; g <= g_last; ++g) {
     const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
@@ -959,18 +966,22 @@ int64_t device_cus() {
   return n;
 }
 
-// Split decision for the bf16 kernel (one workgroup per CU fits in LDS): with
-// `items` query tiles of nku key tiles each, a plain launch takes
-// ceil(items / ncu) * nku tile-times; a split launch takes upw =
-// ceil(items * nku / ncu) plus a fixed cost for the partial records and the
-// merge launch, about 4 tile-times at D = 128 and twice that at D = 64 (a
-// tile costs half as much; measured on MI355X: ~4 us per tile-time at
-// D = 128, ~15 us of fixed cost).  Returns upw when the split pays by 1.3x,
-// else 0.
-int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D) {
+// Split decision for the bf16 kernel, per CU: with `items` query tiles of
+// nku key tiles each, a plain launch takes ceil(items / ncu) * nku
+// tile-times; a split launch takes upw = ceil(items * nku / ncu) plus a
+// fixed cost for the partial records and the merge launch, about 4
+// tile-times at D = 128 and twice that at D = 64 (a tile costs half as much;
+// measured on MI355X: ~4-5 us per tile-time at D = 128, ~15 us of fixed
+// cost).  With a user mask the units differ in cost (empty tiles are free),
+// so ranges stay shorter than an item (at most two segments), where the split
+// still bounds the critical path.  Returns upw when the split pays by 1.3x,
+// else 0: the model overprices a plain launch's last, partly filled round
+// (its CUs then run faster), e.g. the long_hires share, 688 query tiles,
+// measured 1.7 % slower split at a predicted 1.11x.
+int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D, bool masked) {
   if (items <= 0 || nku < 2 || ncu <= 0) return 0;
   const int64_t upw = div_up(items * nku, ncu);
-  if (upw >= nku) return 0;
+  if (masked && upw >= nku) return 0;
   const int64_t plain = div_up(items, ncu) * nku;
   const int64_t fixed = 4 * 128 / D;
   return plain * 10 >= (upw + fixed) * 13 ? upw : 0;
@@ -1013,7 +1024,7 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   if (dtype == SP_BF16 && (D == 64 || D == 128)) {
     const int64_t ncu = device_cus();
     const int64_t items = div_up(Tq, bf16_rows(D)) * Hl * B * R;
-    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D)) split = split_bytes(ncu, D);
+    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D, has_mask != 0)) split = split_bytes(ncu, D);
   }
   return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
 }
@@ -1082,7 +1093,7 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (dtype == SP_BF16) {
     const int64_t ncu = device_cus();
     const int64_t nku = div_up(a.kv_end, KT);
-    const int64_t upw = split_units_per_wg(nwg, nku, ncu, D);
+    const int64_t upw = split_units_per_wg(nwg, nku, ncu, D, has_mask);
     // the split runs only with room for its partial records after the mask
     // part (as sized by sp_masked_attention_workspace_size); otherwise the
     // plain launch runs

@@ -122,7 +122,6 @@ def test_validation_returns_before_launch(lib):
 
 def test_workspace_size(lib):
     from sequence_attention_video_amd import binding as b
-    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == 0
     # one class byte per (384-row, 64-key) tile of the mask (17 x 97 of them),
     # padded to 256 bytes, then one 64-bit word per mask row and 64-key tile
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, True, 0) == \
@@ -135,11 +134,21 @@ def test_workspace_size(lib):
     # two records of 384 rows x (128 + 2) floats per workgroup.
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == \
         2 * 256 * 384 * 130 * 4
-    # all eight shares fill the GPU; the cross share's 8 key tiles are too few
-    # to pay for the merge; the fp32 kernel never splits
+    # all eight shares fill the GPU evenly (512 query tiles, two per CU); the
+    # cross share's 8 key tiles are too few to pay for the merge; the fp32
+    # kernel never splits
     assert b.sp_masked_attention_workspace_size(8, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == 0
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 1024, 4, 64, b.SP_BF16, False, 0) == 0
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 6144, 4, 64, b.SP_F32, False, 0) == 0
+    # 544 query tiles of 49 key tiles take three rounds of 256 CUs unsplit and
+    # 105 tiles per CU split, so eight shares of the 6152-token workload split
+    # when no user mask makes the tiles' costs uneven
+    assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == \
+        2 * 256 * 384 * 130 * 4
+    # the long_hires share, 688 query tiles of 256 key tiles, would gain less
+    # than the 1.3x the split asks for (three rounds unsplit, 688 + 4 tiles
+    # per CU split)
+    assert b.sp_masked_attention_workspace_size(1, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == 0
 
 
 def test_fast_division_host_twin(tmp_path):

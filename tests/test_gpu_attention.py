@@ -123,6 +123,36 @@ def test_attention_split_launch_matches_oracle(D, R, B, Tq, Tk, Hl, kv, mask):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("D,Tq,Tk,Hl,kv", [
+    (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles, ranges of 38 tiles
+    (64, 600, 4000, 100, 4000),     # 300 query tiles of 32 key tiles, ranges of 38 (two workgroups per CU)
+])
+def test_attention_split_ranges_spanning_items(D, Tq, Tk, Hl, kv):
+    """More query tiles than CUs, unevenly: the split's ranges cover whole
+    items (written directly) and pieces of others (merged from records).  The
+    oracle checks a sample of heads holding both kinds; every other row is
+    checked to be finite and written."""
+    say("attention split spanning items", D, Tq, Tk, Hl, kv)
+    ws = sp.sp_masked_attention_workspace_size(1, 1, Tq, Tk, Hl, D, sp.SP_BF16, False, 0)
+    assert ws > 0
+    rng = np.random.default_rng(Tq + Hl)
+    q = rand_bits(rng, (1, 1, Tq, Hl, D), "bf16")
+    k = rand_bits(rng, (1, 1, Tk, Hl, D), "bf16")
+    v = rand_bits(rng, (1, 1, Tk, Hl, D), "bf16")
+    o = sentinel_like((1, 1, Tq, Hl, D), torch.bfloat16)
+    st = lambda T: stacked(1, 1, T, Hl, D)
+    sp.sp_masked_attention(to_dev(q), to_dev(k), to_dev(v), o, 1, 1, Tq, Tk, Hl, D, st(Tq), st(Tk), st(Tk), st(Tq),
+                           kv_valid_len=kv, workspace=torch.empty(ws, dtype=torch.uint8, device="cuda"))
+    torch.cuda.synchronize()
+    got = raw(o)
+    assert np.isfinite(f64(got)).all()
+    heads = [0, 1, 2, Hl // 2, Hl // 2 + 1, Hl - 2, Hl - 1]
+    want = O.attention_heads(f64(q[0][:, :, heads]), f64(k[0][:, :, heads]), f64(v[0][:, :, heads]),
+                             1 / math.sqrt(D), kv)
+    err = np.max(np.abs(f64(got[0][:, :, heads]) - want))
+    assert err <= TOL["bf16"], err
+
+
 def test_attention_single_visible_key_is_exact():
     """One visible key per row: p = 1 and the sum is 1, so o equals that V row
     bit for bit, also through bf16 MFMA."""
