@@ -144,12 +144,14 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * workspace: device scratch of sp_masked_attention_workspace_size() bytes,
  * 256-byte aligned, rewritten by every call; may be NULL when that size is 0.
  * With a mask it holds per-tile mask classes and bit-packed mask rows and is
- * required.  Without a mask (bf16 only) it holds the float32 partial results
- * of a split launch: when the query tiles are too few to fill the GPU (one
- * rank's share of a few heads), the key range of every tile is spread over
- * all compute units and a second kernel merges the partial results.  Without
- * it (NULL or smaller) the same call runs unsplit: same result up to float32
- * summation order, slower on such shapes.
+ * required.  For bf16 it may also hold, after that part, the float32 partial
+ * results of a split launch: when the query tiles do not spread evenly over
+ * the GPU (one rank's share of a few heads, or a count a little above a
+ * multiple of the compute units), the key tiles of all query tiles are cut
+ * into one equal range per compute unit and a second kernel merges the
+ * partial results.  Without room for them (NULL or a smaller workspace) the
+ * same call runs unsplit: same result up to float32 summation order, slower
+ * on such shapes.
  * Supported: SP_BF16 with D in {64, 128} (bf16 MFMA, float32 softmax and
  * accumulation, output rounded to nearest even) and SP_F32 with D in
  * {16, 64, 128} (float32 MFMA throughout).
@@ -157,7 +159,8 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * enough workspace -> SP_ERR_INVALID_ARG; other D, or (bf16) a K or V token
  * stride above 8 million elements (its 32-bit tile offsets), or (bf16) a user
  * mask with Tk above 4096 * 64 keys (the per-row tile classes it keeps in
- * LDS) -> SP_ERR_UNSUPPORTED.
+ * LDS), or a user mask with B above 65535 or Tq above 65535 query tiles
+ * (tiles of 256 rows for bf16 at D = 64, else 384) -> SP_ERR_UNSUPPORTED.
  */
 size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
                                           sp_dtype dtype, int32_t has_mask, int64_t mask_batch_stride);
