@@ -110,6 +110,18 @@ def test_validation_returns_before_launch(lib):
     tk = 4096 * 64 + 1
     assert lib.sp_masked_attention(qa, st, ka, st, va, st, oa, st, 1, 1, 64, tk, 4, 128, b.SP_BF16, tk,
                                    ctypes.c_void_p(5 << 40), 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+    # a user mask beyond the classifier's grid: more than 65535 batches with
+    # per-batch masks, or more than 65535 class-tile rows of queries
+    wsp = ctypes.c_void_p(6 << 40)
+    nb = 65536
+    bst = A(0, 64 * 4 * 128, 512, 128)
+    need = lib.sp_masked_attention_workspace_size(1, nb, 64, 64, 4, 128, b.SP_BF16, 1, 64 * 64)
+    assert lib.sp_masked_attention(qa, bst, ka, bst, va, bst, oa, bst, 1, nb, 64, 64, 4, 128, b.SP_BF16, 64,
+                                   ctypes.c_void_p(5 << 40), 64 * 64, 0.1, wsp, need, None) == b.SP_ERR_UNSUPPORTED
+    tq = 65536 * 384
+    need = lib.sp_masked_attention_workspace_size(1, 1, tq, 64, 4, 128, b.SP_BF16, 1, 0)
+    assert lib.sp_masked_attention(qa, st, ka, st, va, st, oa, st, 1, 1, tq, 64, 4, 128, b.SP_BF16, 64,
+                                   ctypes.c_void_p(5 << 40), 0, 0.1, wsp, need, None) == b.SP_ERR_UNSUPPORTED
     # empty problems are a no-op success
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 0, 64, 1, 128, b.SP_BF16, 64,
                                    None, 0, 0.1, None, 0, None) == b.SP_OK
