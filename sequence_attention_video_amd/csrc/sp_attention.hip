@@ -81,7 +81,8 @@ constexpr int KT = 128;              // keys per LDS tile of the bf16 kernel (a 
 constexpr int NBUF = 2;              // LDS tile buffers of the bf16 kernel (pipeline depth)
 static_assert(kClsRowsF32 % BM32 == 0, "an fp32 query tile lies inside one class tile");
 constexpr float kRescaleSlack = 8.0f;  // log2 units: p <= 2^8 between rescales (fp32 kernel)
-constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports
+constexpr int kMaxClassTiles = 4096;   // BN-key class tiles per mask row the bf16 kernel supports (even)
+static_assert(kMaxClassTiles % 2 == 0, "class rows are padded to even length in place");
 constexpr float kSumLimit = 256.0f;    // bf16 kernel: p <= (sum of a lane's part) <= 256 between rescales
 
 enum : uint8_t { kTileEmpty = 0, kTileFull = 1, kTilePartial = 2 };
@@ -228,7 +229,10 @@ void attn_bf16_kernel(AttnArgs a) {
   // class bytes of this query tile's row of the class map (user masks): read
   // from LDS, so that looking up a tile's class never waits on global memory
   // (a wait for a global load would also wait for the K/V tile in flight)
-  __shared__ uint8_t cls_lds[MASK ? kMaxClassTiles : 4];
+  // (padded with one kTileEmpty byte to even length, so that a key tile
+  // always reads both of its class bytes as one 16-bit word; kMaxClassTiles
+  // is even, and the array is sized to keep two D = 64 workgroups in LDS)
+  __shared__ __attribute__((aligned(4))) uint8_t cls_lds[MASK ? kMaxClassTiles : 4];
   // visibility words of the key tiles in flight (partial tiles only): buffer i
   // holds, for each BN-key class tile c of its key tile, the words of this
   // workgroup's BM rows at [c * BM + row]; filled by direct loads with K/V
@@ -310,29 +314,44 @@ void attn_bf16_kernel(AttnArgs a) {
     const int64_t bm = a.mask_bs ? tc.b : 0;
     cls_row = a.cls + (bm * a.nqt_cls + tc.qt) * int64_t(a.nkt);
     wbase = a.bits + bm * a.nkt * a.ldw;
-    for (int i = tid; i < a.nkt; i += THREADS) cls_lds[i] = cls_row[i];
+    // (the split kernel instead masks the byte past an odd-length row where
+    // it reads it: with the padding copy its register allocation moved Q
+    // fragments to scratch inside the tile loop)
+    if constexpr (SPLIT) {
+      for (int i = tid; i < a.nkt; i += THREADS) cls_lds[i] = cls_row[i];
+    } else {
+      for (int i = tid; i < a.nkt + (a.nkt & 1); i += THREADS) cls_lds[i] = i < a.nkt ? cls_row[i] : uint8_t(kTileEmpty);
+    }
     __syncthreads();
   }
   // Key tiles of KT keys; with a user mask a tile's class combines the classes
   // of its BN-key class tiles, and empty tiles are skipped.  This segment runs
   // tiles [kt_first, nkt_eff).
   const int nkt_eff = SPLIT ? kt_stop : int((a.kv_end + KT - 1) / KT);
+  // The class of a key tile is read once, when the tile enters the pipeline
+  // (right after the barrier, with no operand reads in flight), and carried
+  // with it: each class read is an LDS round trip that the wave waits for
+  // (-3 % on fully masked launches with the carry).  The split kernel, with
+  // its segment state, reads the class again where it is used: there the
+  // carried values push the Q fragments out to scratch (+3.5 %).
+  constexpr bool kCarryClass = !SPLIT;
+  static_assert(KT / BN == 2 && kTileEmpty == 0 && kTileFull == 1, "two class bytes per key tile");
   auto tile_class = [&](int kt) __attribute__((always_inline)) -> uint8_t {
     if (!MASK) return kTileFull;
-    bool any = false, all = true;
-#pragma unroll
-    for (int i = 0; i < KT / BN; ++i) {
-      const int c = kt * (KT / BN) + i;
-      const uint8_t v = c < a.nkt ? cls_lds[c] : uint8_t(kTileEmpty);
-      any |= v != kTileEmpty;
-      all &= v == kTileFull;
-    }
-    return !any ? kTileEmpty : (all ? kTileFull : kTilePartial);
+    // uniform over the workgroup: kept in scalar registers
+    uint32_t pair = __builtin_amdgcn_readfirstlane(*reinterpret_cast<const uint16_t*>(cls_lds + 2 * kt));
+    if (SPLIT && 2 * kt + 1 >= a.nkt) pair &= 0xffu;
+    return pair == 0 ? kTileEmpty : (pair == 0x0101u ? kTileFull : kTilePartial);
   };
-  auto next_tile = [&](int kt) __attribute__((always_inline)) {
+  // next tile after kt that is not empty (nkt_eff or more if none), and its class
+  auto next_tile = [&](int kt, uint8_t& c) __attribute__((always_inline)) {
     ++kt;
+    c = kTileFull;
     if (MASK)
-      while (kt < nkt_eff && tile_class(kt) == kTileEmpty) ++kt;
+      for (; kt < nkt_eff; ++kt) {
+        c = tile_class(kt);
+        if (c != kTileEmpty) break;
+      }
     return kt;
   };
 
@@ -417,8 +436,8 @@ void attn_bf16_kernel(AttnArgs a) {
   constexpr int WROWS = 2 * 64;                       // rows per wave-wide load
   constexpr int WLOADS = (KT / BN) * (BM / WROWS);
   static_assert(BM % WROWS == 0 && WLOADS <= WAVES, "one word load per wave");
-  auto issue_words = [&](int kt, uint64_t* dst) __attribute__((always_inline)) {
-    if (!MASK || kt >= nkt_eff || wu >= WLOADS || tile_class(kt) != kTilePartial) return;
+  auto issue_words = [&](int kt, uint8_t cls, uint64_t* dst) __attribute__((always_inline)) {
+    if (!MASK || kt >= nkt_eff || wu >= WLOADS || cls != kTilePartial) return;
     const int c = wu / (BM / WROWS), r0 = (wu % (BM / WROWS)) * WROWS;
     const int ncls = a.nkt - kt * (KT / BN) < KT / BN ? a.nkt - kt * (KT / BN) : KT / BN;
     if (c >= ncls) return;
@@ -427,10 +446,10 @@ void attn_bf16_kernel(AttnArgs a) {
     __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(dst + c * BM + r0), 16, 16 * lane,
                                              int32_t((c * a.ldw + int64_t(tc.qt) * BM + r0) * 8), 0, 0);
   };
-  auto compute = [&](int kt, const char* kb_, const char* vb_, const uint64_t* mwl) __attribute__((always_inline)) {
+  auto compute = [&](int kt, uint8_t cls, const char* kb_, const char* vb_, const uint64_t* mwl)
+                     __attribute__((always_inline)) {
     constexpr int NP = KT / 32;   // parts per tile
     const int64_t key0 = int64_t(kt) * KT;
-    const uint8_t cls = tile_class(kt);
     const bool edge = (MASK && cls == kTilePartial) || key0 + KT > a.kv_end;
     // visibility words of this lane's rows for the BN-key class tiles of this tile
     // S^T of part kb (keys x queries).  The K fragment (key 32*kb + l32,
@@ -573,20 +592,22 @@ void attn_bf16_kernel(AttnArgs a) {
   // Iteration i: wait for tile i's loads, barrier (tile i visible to all waves;
   // every wave done with tile i-1), issue tile i+NBUF-1 into tile i-1's
   // buffer, compute tile i.
-  int ahead[NBUF];   // tiles i .. i+NBUF-1
-  ahead[0] = MASK ? next_tile(kt_first - 1) : kt_first;
+  int ahead[NBUF];       // tiles i .. i+NBUF-1
+  uint8_t acls[NBUF];    // and their classes
+  ahead[0] = next_tile(kt_first - 1, acls[0]);
 #pragma unroll
-  for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff);
+  for (int j = 1; j < NBUF; ++j) ahead[j] = next_tile(ahead[j - 1] < nkt_eff ? ahead[j - 1] : nkt_eff, acls[j]);
   constexpr int MWB = (KT / BN) * BM;   // words per mask-word buffer
   if (ahead[0] < nkt_eff) issue(ahead[0], kbuf(I0{}), vbuf(I0{}));
-  issue_words(ahead[0], mw_lds);
+  issue_words(ahead[0], acls[0], mw_lds);
   if constexpr (NBUF > 2) {
     if (ahead[1] < nkt_eff) issue(ahead[1], kbuf(std::integral_constant<int, 1>{}), vbuf(std::integral_constant<int, 1>{}));
-    issue_words(ahead[1], mw_lds + MWB);
+    issue_words(ahead[1], acls[1], mw_lds + MWB);
   }
   auto stage = [&](auto sidx) __attribute__((always_inline)) -> bool {
     constexpr int S = decltype(sidx)::value;
     const int kt = ahead[0];
+    const uint8_t cls = kCarryClass ? acls[0] : uint8_t(0);
     if (kt >= nkt_eff) return false;
     // loads still allowed in flight: those of the tiles issued after tile i
     int later = 0;
@@ -596,12 +617,16 @@ void attn_bf16_kernel(AttnArgs a) {
     else wait_vmem<0>();
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < NBUF - 1; ++j) ahead[j] = ahead[j + 1];
-    ahead[NBUF - 1] = next_tile(ahead[NBUF - 2] < nkt_eff ? ahead[NBUF - 2] : nkt_eff);
+    for (int j = 0; j < NBUF - 1; ++j) {
+      ahead[j] = ahead[j + 1];
+      acls[j] = acls[j + 1];
+    }
+    ahead[NBUF - 1] = next_tile(ahead[NBUF - 2] < nkt_eff ? ahead[NBUF - 2] : nkt_eff, acls[NBUF - 1]);
     using NX = std::integral_constant<int, (S + NBUF - 1) % NBUF>;
     if (ahead[NBUF - 2] < nkt_eff) issue(ahead[NBUF - 2], kbuf(NX{}), vbuf(NX{}));
-    issue_words(ahead[NBUF - 2], mw_lds + NX::value * MWB);
-    if (wave_has_rows) compute(kt, kbuf(sidx), vbuf(sidx), mw_lds + S * MWB);
+    issue_words(ahead[NBUF - 2], kCarryClass ? acls[NBUF - 2] : tile_class(ahead[NBUF - 2]),
+                mw_lds + NX::value * MWB);
+    if (wave_has_rows) compute(kt, kCarryClass ? cls : tile_class(kt), kbuf(sidx), vbuf(sidx), mw_lds + S * MWB);
     return true;
   };
   for (;;) {
