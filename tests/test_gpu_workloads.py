@@ -134,3 +134,40 @@ def test_workload_zero_copy_matches_exchange_path(name):
     Tq = wl.Tq if wl.cross else wl.T_pad
     ot = step.ot.view(wl.W, wl.B, Tq // wl.W, wl.H, wl.D).permute(1, 0, 2, 3, 4).reshape(wl.B, Tq, wl.H, wl.D)
     assert torch.equal(step.oz.view(torch.uint8), ot.contiguous().view(torch.uint8))
+
+
+@pytest.mark.parametrize("name", [n for n in ORDER if n != "tiny"])
+def test_workload_rank_share(name):
+    """One rank's share alone (R = 1), the launch each GPU runs when the ranks
+    are devices and the one bench.py times as the share: split over the GPU
+    where the share has too few query tiles.  Ranks 0 and W-1 on sampled rows
+    against the oracle."""
+    wl = WORKLOADS[name]
+    say("rank share", name)
+    x = make_inputs(wl)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    mask = to_dev(x["mask"]) if x["mask"] is not None else None
+    step = UlyssesStep(wl, q, k, v, mask)
+    step.run()
+    W, Hl, D, T, Tp = wl.W, wl.Hl, wl.D, wl.T, wl.T_pad
+    scale = 1.0 / math.sqrt(D)
+    rng = np.random.default_rng(100 + wl.index)
+    names = ["k", "v"] if wl.cross else ["q", "k", "v"]
+    padded = {n: O.pad_tokens(x[n], Tp) for n in names}
+    heads = {n: O.send_recv_heads(O.token_shards(padded[n], W)) for n in names}
+    mask_ext = O.extend_user_mask(x["mask"], Tp) if x["mask"] is not None else None
+    Tq = wl.Tq if wl.cross else Tp
+    kv_valid = T if mask_ext is None else Tp
+    for r in (0, W - 1):
+        out = torch.empty_like(step.oh[r])
+        out.view(torch.uint8).fill_(0xFF)
+        step.attention_rank(r, out)
+        torch.cuda.synchronize()
+        got = f64(raw(out))
+        assert np.isfinite(got).all()
+        qr = f64(x["q"][:, :, r * Hl:(r + 1) * Hl]) if wl.cross else f64(heads["q"][r])
+        rows = sample_rows(Tq, Tq // W, T if not wl.cross else Tq, rng)
+        want = O.attention_heads(qr, f64(heads["k"][r]), f64(heads["v"][r]), scale, kv_valid, mask_ext,
+                                 rows=rows)[:, rows]
+        err = float(np.max(np.abs(got[:, rows] - want)))
+        assert err <= TOL[wl.dtype], (r, err)
