@@ -316,7 +316,23 @@ def main():
     torch.cuda.synchronize()
     ms_zero = z0.elapsed_time(z1) / args.steps
     zero_equal = bool(torch.equal(step.outz.view(torch.uint8), ref_out.view(torch.uint8)))
-    del ref_out
+
+    # -- the same step recorded once as a HIP graph and replayed (the kernels
+    #    and their arguments are fixed; the per-launch host work and launch
+    #    gaps go); reported beside the step
+    graph = step.capture()
+    for _ in range(max(3, args.warmup // 4)):
+        graph.replay()
+    g0 = torch.cuda.Event(enable_timing=True)
+    g1 = torch.cuda.Event(enable_timing=True)
+    g0.record(stream)
+    for _ in range(args.steps):
+        graph.replay()
+    g1.record(stream)
+    torch.cuda.synchronize()
+    ms_graph = g0.elapsed_time(g1) / args.steps
+    graph_equal = bool(torch.equal(step.out.view(torch.uint8), ref_out.view(torch.uint8)))
+    del graph, ref_out
 
     # -- the 2-D (height x width) split in place of the 1-D token split, for
     #    workloads that are one video grid; reported beside the step
@@ -438,6 +454,8 @@ def main():
         "cp2d_step": cp2d,
         "zero_copy_step": {"ms": round(ms_zero, 4), "TFLOP/s": round(attn_flops / (ms_zero * 1e-3) / 1e12, 2),
                            "output_bytes_equal_to_step": zero_equal},
+        "graph_step": {"ms": round(ms_graph, 4), "TFLOP/s": round(attn_flops / (ms_graph * 1e-3) / 1e12, 2),
+                       "output_bytes_equal_to_step": graph_equal},
         "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),
                                         "mfma_frac": round(share_tflops / peak_mfma, 4), "R": 1,
                                         "split": share_split,

@@ -179,6 +179,21 @@ class UlyssesStep:
         self.gather_output_tokens(lengths)
         return self.out
 
+    def capture(self):
+        """Record run() into a HIP graph (torch.cuda.CUDAGraph) and return it:
+        replay() re-issues the step's kernels on the same buffers with the same
+        arguments, without the per-launch host work.  The library allocates
+        nothing and records no memset, so every node is one of its kernels."""
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()                      # first launches outside the capture
+        torch.cuda.current_stream().wait_stream(side)
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            self.run()
+        return g
+
     # -- the same step with both exchanges folded into attention's addressing --
     # On one device rank r's head-side view is a strided view of the padded
     # token-side tensor: heads r*Hl.. of every token (rank stride Hl*D, token

@@ -171,3 +171,25 @@ def test_workload_rank_share(name):
                                  rows=rows)[:, rows]
         err = float(np.max(np.abs(got[:, rows] - want)))
         assert err <= TOL[wl.dtype], (r, err)
+
+
+@pytest.mark.parametrize("name", ["video_self", "uneven_mask", "cross_v2a", "tiny"])
+def test_workload_step_graph_replays(name):
+    """The step recorded as a HIP graph: every replay, with eager work and
+    synchronisation between replays, writes the same output bytes as the eager
+    step."""
+    wl = WORKLOADS[name]
+    say("graph", name)
+    x = make_inputs(wl)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    mask = to_dev(x["mask"]) if x["mask"] is not None else None
+    step = UlyssesStep(wl, q, k, v, mask)
+    want = step.run().clone()
+    torch.cuda.synchronize()
+    g = step.capture()
+    for i in range(4):
+        step.out.view(torch.uint8).fill_(0xFF)       # eager work between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(step.out.view(torch.uint8), want.view(torch.uint8)), i
