@@ -265,19 +265,26 @@ def main():
     if step.need_pad and mask is not None:
         pad_bytes += mask.shape[0] * (T * T + Tp * Tp)
 
-    # -- warmup, then K timed steps with per-stage events on the launch stream
+    # -- warmup, then K timed steps (events only around the K steps), then the
+    #    same K steps again with per-stage events for the breakdown
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step.run()
     torch.cuda.synchronize()
     stream = torch.cuda.current_stream()
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     log("timed", args.steps)
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     t_start.record(stream)
+    for _ in range(args.steps):
+        step.run()
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_step = t_start.elapsed_time(t_end) / args.steps
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
     for i in range(args.steps):
         e = ev[i]
         e[0].record(stream)
@@ -291,10 +298,7 @@ def main():
         e[3].record(stream)
         step.gather_output_tokens(lengths)
         e[4].record(stream)
-    t_end.record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_step = t_start.elapsed_time(t_end) / args.steps
     stage = lambda a, b: float(np.mean([ev[i][a].elapsed_time(ev[i][b]) for i in range(args.steps)]))
     ms_pad_send = stage(0, 1)
     ms_attn = stage(1, 2)
