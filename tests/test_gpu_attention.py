@@ -225,3 +225,52 @@ def test_attention_large_scores_stay_finite():
     got, want = run_case("bf16", 128, 1, 1, 256, 512, 2, 512, None, seed=6, scale=0.35)
     assert np.isfinite(got).all()
     assert np.max(np.abs(got - want)) <= 2e-2
+
+
+def test_attention_mask_at_widest_class_row():
+    """A user mask over exactly 4096 64-key class tiles (the most the kernel's
+    per-row class map holds) and a few query rows."""
+    say("attention widest mask")
+    R, B, Tq, Hl, D = 1, 1, 40, 1, 64
+    Tk = 4096 * 64
+    rng = np.random.default_rng(7)
+    q = rand_bits(rng, (R, B, Tq, Hl, D), "bf16")
+    k = rand_bits(rng, (R, B, Tk, Hl, D), "bf16")
+    v = rand_bits(rng, (R, B, Tk, Hl, D), "bf16")
+    m = np.zeros((1, Tq, Tk), np.uint8)
+    m[0, :, -700:] = 1                                   # the last class tiles, partly
+    m[0, :, :: 997] = 1                                  # sparse keys everywhere
+    m[0, 3, :] = 0                                       # a row with nothing visible
+    o = sentinel_like((R, B, Tq, Hl, D), torch.bfloat16)
+    sp.sp_masked_attention(to_dev(q), to_dev(k), to_dev(v), o, R, B, Tq, Tk, Hl, D, stacked(R, B, Tq, Hl, D),
+                           stacked(R, B, Tk, Hl, D), stacked(R, B, Tk, Hl, D), stacked(R, B, Tq, Hl, D),
+                           mask=to_dev(m))
+    torch.cuda.synchronize()
+    got = f64(raw(o))
+    want = O.attention_heads(f64(q[0]), f64(k[0]), f64(v[0]), 1 / math.sqrt(D), Tk, m)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got[0] - want)) <= TOL["bf16"]
+
+
+def test_attention_largest_key_token_stride():
+    """K and V rows 8,000,000 elements apart (near the 32-bit byte offsets of
+    one key tile), read through a ragged last tile."""
+    say("attention largest stride")
+    B, Tq, Tk, Hl, D = 1, 70, 3, 1, 128
+    st_k = 8_000_000
+    rng = np.random.default_rng(8)
+    q = rand_bits(rng, (1, B, Tq, Hl, D), "bf16")
+    kk = rand_bits(rng, (Tk, D), "bf16")
+    vv = rand_bits(rng, (Tk, D), "bf16")
+    kbuf = torch.zeros(Tk * st_k, dtype=torch.bfloat16, device="cuda")
+    vbuf = torch.zeros(Tk * st_k, dtype=torch.bfloat16, device="cuda")
+    kbuf.view(Tk, st_k)[:, :D] = to_dev(kk)
+    vbuf.view(Tk, st_k)[:, :D] = to_dev(vv)
+    o = sentinel_like((1, B, Tq, Hl, D), torch.bfloat16)
+    sts = (Tk * st_k, Tk * st_k, st_k, D)
+    sp.sp_masked_attention(to_dev(q), kbuf, vbuf, o, 1, B, Tq, Tk, Hl, D, stacked(1, B, Tq, Hl, D), sts, sts,
+                           stacked(1, B, Tq, Hl, D))
+    torch.cuda.synchronize()
+    got = f64(raw(o))[0]
+    want = O.attention_heads(f64(q[0]), f64(kk)[None, :, None, :], f64(vv)[None, :, None, :], 1 / math.sqrt(D), Tk)
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
