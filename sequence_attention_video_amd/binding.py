@@ -39,10 +39,6 @@ class AttnStrides(ctypes.Structure):
                 ("token", ctypes.c_int64), ("head", ctypes.c_int64)]
 
 
-class SpError(Exception):
-    pass
-
-
 _lib = None
 
 
