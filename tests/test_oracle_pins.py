@@ -11,10 +11,8 @@ oracle and shows that these checks catch each one.
 import math
 
 import numpy as np
-import pytest
 
 import oracle as O
-from tests.conftest import load_golden
 from tests import pin_checks as P
 
 
