@@ -46,6 +46,7 @@
 //     split the key range over all compute units and merge partial results
 //     (attn_combine_kernel).
 
+#include "sp_bits.h"
 #include "sp_internal.h"
 
 #include <cmath>
@@ -879,49 +880,86 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- mask tiles
 
-// One workgroup per (batch, q-tile, k-tile), mask rows spread over threads: reads
-// the row's BN bytes of the tile (as wide as their alignment allows), writes
-// them as one 64-bit visibility word (bit j = key BN*kt + j), and records
-// whether none, all, or some of the tile's in-range bytes are set.
-__device__ __forceinline__ uint64_t nonzero_bytes_to_bits(uint64_t x) {
-  // bit j of the result = (byte j of x != 0)
-  uint64_t r = 0;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) r |= uint64_t(((x >> (8 * j)) & 0xffu) != 0) << j;
-  return r;
-}
+// One workgroup (16 waves) per (batch, block of `rows` mask rows, kClsSpan
+// class tiles of BN keys).  Wave w takes rows w, w + 16, ..., kClsUnroll rows
+// at a time (their loads in flight together); on a row, lane l reads the 8
+// mask bytes of keys 8l .. 8l+7 of the span (the wave reads 512 contiguous
+// bytes of the row) and stores their 8 visibility bits as byte l % 8 of the
+// row's word of class tile l / 8 in LDS (bit j of a word = key BN*kt + j).
+// The words then go out class tile by class tile, rows contiguous, and a
+// class tile is empty, full or partial by the OR / AND of its words (keys
+// past Tk count as absent).  Reading whole 512-byte row pieces keeps every
+// fetched line in one workgroup: one workgroup per 64-byte class tile made
+// neighbouring workgroups (often on other XCDs) fetch the same lines, 2.9x the
+// mask bytes from HBM.
+constexpr int kClsSpan = 8;          // class tiles per classifier workgroup
+constexpr int kClsMaxRows = 384;     // largest class-tile height
+constexpr int kClsThreads = 1024;    // classifier workgroup
+constexpr int kClsUnroll = 4;        // rows per wave whose loads are in flight together
+static_assert(kRows<64> <= kClsMaxRows && kRows<128> <= kClsMaxRows && kClsRowsF32 <= kClsMaxRows,
+              "every class-tile height fits the classifier's row stage");
 
-__global__ __launch_bounds__(kThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
-                                                               int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
-                                                               uint64_t* bits, int64_t ldw, int32_t rows) {
-  static_assert(BN == 64, "one 64-bit word per row and tile");
-  const int kt = blockIdx.x, qt = blockIdx.y;
+__global__ __launch_bounds__(kClsThreads) void classify_mask_kernel(const uint8_t* mask, int64_t mask_bs, int64_t Tq,
+                                                                  int64_t Tk, int32_t nqt, int32_t nkt, uint8_t* cls,
+                                                                  uint64_t* bits, int64_t ldw, int32_t rows) {
+  static_assert(BN == 64, "one 64-bit word per row and class tile");
+  constexpr int kWavesC = kClsThreads / 64;
+  __shared__ uint64_t words[kClsSpan * kClsMaxRows];   // [class tile][row]
+  __shared__ int any_s[kClsSpan], all_s[kClsSpan];
+  const int span = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
-  const int64_t col0 = int64_t(kt) * BN;
-  const int n = int(Tk - col0 < BN ? Tk - col0 : BN);           // in-range keys of the tile
-  const uint64_t full = n == 64 ? ~0ull : ((1ull << n) - 1);
-  int any = 0, all = 1;
-  for (int r = threadIdx.x; r < rows; r += kThreads) {
-    const int64_t row = int64_t(qt) * rows + r;
-    if (row >= Tq) break;
-    const uint8_t* p = mask + b * mask_bs + row * Tk + col0;
-    uint64_t word = 0;
-    if (n == BN && (reinterpret_cast<uintptr_t>(p) & 7) == 0) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) word |= nonzero_bytes_to_bits(reinterpret_cast<const uint64_t*>(p)[i]) << (8 * i);
-    } else if (n == BN && (reinterpret_cast<uintptr_t>(p) & 3) == 0) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) word |= nonzero_bytes_to_bits(reinterpret_cast<const uint32_t*>(p)[i]) << (4 * i);
-    } else {
-      for (int c = 0; c < n; ++c) word |= uint64_t(p[c] != 0) << c;
-    }
-    bits[(b * nkt + kt) * ldw + row] = word;   // rows contiguous per class tile
-    any |= word != 0;
-    all &= word == full;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int c = lane >> 3;                                   // this lane's class tile in the span
+  const int64_t key = (int64_t(span) * kClsSpan + c) * BN + 8 * (lane & 7);   // first of its 8 keys
+  const int nv = int(Tk - key <= 0 ? 0 : (Tk - key < 8 ? Tk - key : 8));
+  const bool aligned8 = ((reinterpret_cast<uintptr_t>(mask) | uintptr_t(mask_bs) | uintptr_t(Tk)) & 7) == 0;
+  const int64_t left = Tq - int64_t(qt) * rows;
+  const int nrows = int(left < rows ? left : rows);
+  if (threadIdx.x < kClsSpan) {
+    any_s[threadIdx.x] = 0;
+    all_s[threadIdx.x] = 1;
   }
-  any = __syncthreads_or(any);
-  all = __syncthreads_and(all);
-  if (threadIdx.x == 0) cls[(b * nqt + qt) * int64_t(nkt) + kt] = !any ? kTileEmpty : (all ? kTileFull : kTilePartial);
+  uint8_t* wbytes = reinterpret_cast<uint8_t*>(words);
+  const uint8_t* base = mask + b * mask_bs + int64_t(qt) * rows * Tk + key;
+  for (int r0 = w; r0 < nrows; r0 += kWavesC * kClsUnroll) {
+    uint64_t x[kClsUnroll];
+#pragma unroll
+    for (int u = 0; u < kClsUnroll; ++u) {
+      const int r = r0 + u * kWavesC;
+      x[u] = 0;
+      if (r < nrows) {
+        const uint8_t* p = base + int64_t(r) * Tk;
+        if (nv == 8 && aligned8) {
+          x[u] = *reinterpret_cast<const uint64_t*>(p);
+        } else {
+          for (int i = 0; i < nv; ++i) x[u] |= uint64_t(p[i]) << (8 * i);
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kClsUnroll; ++u) {
+      const int r = r0 + u * kWavesC;
+      if (r < nrows) wbytes[(c * kClsMaxRows + r) * 8 + (lane & 7)] = uint8_t(nonzero_bytes_to_bits8(x[u]));
+    }
+  }
+  __syncthreads();
+  // words out, rows contiguous per class tile; the classes by OR / AND (every
+  // writer of a flag writes the same value, so plain stores suffice)
+  for (int i = threadIdx.x; i < kClsSpan * nrows; i += kClsThreads) {
+    const int ci = i / nrows, r = i - ci * nrows;
+    const int cti = span * kClsSpan + ci;
+    if (cti >= nkt) continue;
+    const uint64_t word = words[ci * kClsMaxRows + r];
+    bits[(b * nkt + cti) * ldw + int64_t(qt) * rows + r] = word;
+    const int64_t n = Tk - int64_t(cti) * BN < BN ? Tk - int64_t(cti) * BN : BN;   // in-range keys
+    const uint64_t full = n >= 64 ? ~0ull : ((1ull << n) - 1);
+    if (word != 0) any_s[ci] = 1;
+    if (word != full) all_s[ci] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x < kClsSpan && span * kClsSpan + int(threadIdx.x) < nkt)
+    cls[(b * nqt + qt) * int64_t(nkt) + span * kClsSpan + threadIdx.x] =
+        !any_s[threadIdx.x] ? kTileEmpty : (all_s[threadIdx.x] ? kTileFull : kTilePartial);
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -1132,7 +1170,8 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   hipStream_t s = as_stream(stream);
   if (has_mask) {
     const int64_t bm = mask_batch_stride ? B : 1;
-    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(nkt), unsigned(nqt_cls), unsigned(bm)), dim3(kThreads), 0,
+    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(div_up(nkt, kClsSpan)), unsigned(nqt_cls), unsigned(bm)),
+                       dim3(kClsThreads), 0,
                        s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
                        static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw, int32_t(crows));
     if (launch_status() != SP_OK) return SP_ERR_HIP;

@@ -203,6 +203,53 @@ int main() {
     assert res.returncode == 0 and res.stdout.strip() == "0", res.stdout
 
 
+def test_mask_bit_packing_host_twin(tmp_path):
+    """The byte-to-bit packing of the mask classifier against a byte-by-byte
+    loop.  Bytes cannot carry into each other (each adds at most 0x7f to its
+    low 7 bits), so every value of each byte against a set of values of the
+    other three covers the 32-bit packing; sampled 64-bit inputs check the
+    two halves' placement."""
+    gxx = shutil.which("g++")
+    if gxx is None:
+        pytest.skip("g++ not available")
+    src = tmp_path / "bits.cpp"
+    src.write_text(r"""
+#include "sp_bits.h"
+#include <cstdio>
+#include <cstdint>
+static uint64_t slow(uint64_t x, int n) {
+  uint64_t r = 0;
+  for (int j = 0; j < n; ++j) r |= uint64_t(((x >> (8 * j)) & 0xff) != 0) << j;
+  return r;
+}
+int main() {
+  uint64_t bad = 0, x = 88172645463325252ull;
+  const uint32_t others[] = {0, 1, 2, 0x40, 0x7f, 0x80, 0x81, 0xfe, 0xff};
+  for (int pos = 0; pos < 4; ++pos)
+    for (uint32_t v = 0; v < 256; ++v)
+      for (uint32_t a : others) for (uint32_t b : others) for (uint32_t c : others) {
+        const uint32_t o[3] = {a, b, c};
+        uint32_t w = 0;
+        for (int q = 0, k = 0; q < 4; ++q) w |= (q == pos ? v : o[k++]) << (8 * q);
+        bad += sp::nonzero_bytes_to_bits4(w) != slow(w, 4);
+      }
+  for (int i = 0; i < 1000000; ++i) {
+    x ^= x << 13; x ^= x >> 7; x ^= x << 17;
+    uint64_t y = x & (x >> 3) & (x >> 5);   // sparse bytes: many zero bytes
+    bad += sp::nonzero_bytes_to_bits8(x) != slow(x, 8);
+    bad += sp::nonzero_bytes_to_bits8(y) != slow(y, 8);
+  }
+  printf("%llu\n", (unsigned long long)bad);
+  return bad != 0;
+}
+""")
+    exe = tmp_path / "bits"
+    subprocess.run([gxx, "-O2", "-std=c++17", "-I", os.path.join(ROOT, "sequence_attention_video_amd", "csrc"),
+                    str(src), "-o", str(exe)], check=True)
+    res = subprocess.run([str(exe)], capture_output=True, text=True)
+    assert res.returncode == 0 and res.stdout.strip() == "0", res.stdout
+
+
 def test_bench_refuses_more_than_one_gpu():
     """bench.py measures one GPU; --gpus N > 1 exits with a message (no GPU touched)."""
     import sys
