@@ -274,3 +274,31 @@ def test_attention_largest_key_token_stride():
     got = f64(raw(o))[0]
     want = O.attention_heads(f64(q[0]), f64(kk)[None, :, None, :], f64(vv)[None, :, None, :], 1 / math.sqrt(D), Tk)
     assert np.max(np.abs(got - want)) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_attention_rising_scores_rescale_often(D):
+    """Scores that rise along the keys (by up to 40 over 700 keys, in natural
+    units, with noise) push the running max up part after part: the kernel's
+    slow path (raise the max, rescale O and l, recompute the part) runs
+    again and again, up to a key padding edge inside the last tile."""
+    say("attention rising scores", D)
+    rng = np.random.default_rng(11 + D)
+    R, B, Tq, Tk, Hl = 1, 1, 200, 700, 2
+    qf = np.zeros((R, B, Tq, Hl, D), np.float32)
+    qf[..., 0] = 1.0
+    qf[..., 1:] = 0.05 * rng.standard_normal((R, B, Tq, Hl, D - 1))
+    kf = 0.05 * rng.standard_normal((R, B, Tk, Hl, D)).astype(np.float32)
+    kf[..., 0] = (np.arange(Tk, dtype=np.float32) * (40.0 / Tk))[None, None, :, None]
+    from sequence_attention_video_amd.workloads import f32_to_bf16_bits
+    q, k = f32_to_bf16_bits(qf), f32_to_bf16_bits(kf)
+    v = rand_bits(rng, (R, B, Tk, Hl, D), "bf16")
+    st_q, st_k = stacked(R, B, Tq, Hl, D), stacked(R, B, Tk, Hl, D)
+    o = sentinel_like((R, B, Tq, Hl, D), torch.bfloat16)
+    sp.sp_masked_attention(to_dev(q), to_dev(k), to_dev(v), o, R, B, Tq, Tk, Hl, D, st_q, st_k, st_k, st_q,
+                           kv_valid_len=690, scale=1.0)
+    torch.cuda.synchronize()
+    got = f64(raw(o))
+    want = O.attention_heads(f64(q[0]), f64(k[0]), f64(v[0]), 1.0, 690)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got[0] - want)) <= TOL["bf16"]
