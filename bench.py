@@ -102,6 +102,134 @@ def traffic_probe(workload: str, launches: int = 3):
     print("traffic probe done", workload, flush=True)
 
 
+def mfma_probe(workload: str, launches: int = 3):
+    """Run only what the MFMA counter pass measures: the step once, then the
+    all-ranks attention launch `launches` times and rank 0's share alone
+    (R = 1, split when the library splits it) `launches` + 1 times."""
+    import numpy as np
+    import torch
+
+    from sequence_attention_video_amd import binding
+    from sequence_attention_video_amd.pipeline import UlyssesStep
+    from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
+    wl = WORKLOADS[workload]
+    x = make_inputs(wl)
+    td = lambda a: (torch.from_numpy(a).view(torch.bfloat16) if a.dtype == np.uint16 else torch.from_numpy(a)).cuda()
+    step = UlyssesStep(wl, td(x["q"]), td(x["k"]), td(x["v"]), td(x["mask"]) if x["mask"] is not None else None)
+    step.run()
+    for _ in range(launches):
+        step.attention()
+    tq = wl.q_tokens_pad if wl.cross else wl.T_pad
+    need = binding.sp_masked_attention_workspace_size(1, wl.B, tq, wl.T_pad, wl.Hl, wl.D,
+                                                      binding._dtype_code(step.kh), step.mask is not None, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    share_out = torch.empty_like(step.oh[0])
+    for _ in range(launches + 1):
+        step.attention_rank(0, share_out, ws)
+    torch.cuda.synchronize()
+    print("mfma probe done", workload, flush=True)
+
+
+def attention_flops(wl) -> tuple:
+    """Algorithmic attention flops (4*D per visible (query, key) pair and
+    head, over every query row the path computes): (all W shares, one share)."""
+    if wl.cross:
+        pairs = wl.q_tokens_pad * wl.T
+    elif wl.mask == "block_causal":
+        from sequence_attention_video_amd.workloads import make_inputs
+        m = make_inputs(wl)["mask"]
+        pairs = int(m.astype("int64").sum()) // m.shape[0] + (wl.T_pad - wl.T) * wl.T   # pad rows see real keys
+    else:
+        pairs = wl.T_pad * wl.T
+    total = 4 * wl.D * wl.H * wl.B * pairs
+    return total, total // wl.W
+
+
+MFMA_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_BUSY_CU_CYCLES", "GRBM_GUI_ACTIVE"]
+N_XCD, N_SIMD, PEAK_CLOCK_GHZ = 8, 1024, 2.4     # MI355X: 256 CUs x 4 SIMDs, published peak clock
+
+
+def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
+    """Turn one rocprofv3 --pmc pass over `bench.py --mfma-probe` into
+    profiles/attention_mfma_<workload>.md.  Per attention launch kind: the
+    MFMA flops the hardware executed (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512)
+    against the algorithmic flops; MFMA busy cycles per SIMD
+    (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs) over the launch's duration at the
+    published 2.4 GHz (utilisation in the terms of the published peak) and
+    over the cycles the GPU was active (GRBM_GUI_ACTIVE, counted once per
+    XCD: the clock the launch actually ran at)."""
+    import collections
+
+    from sequence_attention_video_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
+    flops_all, flops_share = attention_flops(wl)
+    per = collections.defaultdict(dict)
+    kname, dur = {}, {}
+    for r in _counter_rows(pmc_dir):
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        m = re.search(r"(attn_\w+<[^>]*>|\w+_kernel)\(", r["Kernel_Name"])
+        kname[d] = m.group(1) if m else r["Kernel_Name"][:60]
+        dur[d] = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) * 1e-9
+    order = sorted(per)
+    main = [d for d in order if kname[d].startswith("attn_") and "combine" not in kname[d]]
+    # dispatch order of the probe: the step's attention launch, `n` all-ranks
+    # launches, then n + 1 share launches (a split share runs a merge kernel
+    # after each); the first launch of each kind is left out (cold)
+    n = (len(main) - 2) // 2
+    share = main[2 + n:]
+    groups = [("all W rank shares (one launch)", main[1:1 + n], flops_all),
+              ("rank 0's share alone (R = 1)", share, flops_share)]
+    merge = [d for d in order if "combine" in kname[d] and d > main[1 + n]][1:]
+    rows, recs = [], []
+    for label, ds, flops in groups:
+        avg = lambda f: sum(f(d) for d in ds) / len(ds)
+        busy = avg(lambda d: per[d]["SQ_VALU_MFMA_BUSY_CYCLES"]) / N_SIMD
+        hw = avg(lambda d: per[d]["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
+        t = avg(lambda d: dur[d])
+        gui = avg(lambda d: per[d]["GRBM_GUI_ACTIVE"]) / N_XCD
+        util_peak = busy / (t * PEAK_CLOCK_GHZ * 1e9)
+        util_active = busy / gui
+        rec = {"launch": label, "kernel": kname[ds[0]], "launches": len(ds), "us_per_launch": round(t * 1e6, 1),
+               "algorithmic_flops": int(flops), "hw_mfma_flops": int(hw), "hw_over_algorithmic": round(hw / flops, 4),
+               "mfma_busy_cycles_per_simd": int(busy), "mfma_util_at_peak_clock": round(util_peak, 4),
+               "mfma_busy_of_active_cycles": round(util_active, 4), "active_cycles_per_xcd": int(gui),
+               "implied_clock_ghz": round(gui / t / 1e9, 3)}
+        if label.startswith("rank") and merge:
+            rec["merge_kernel_us"] = round(sum(dur[d] for d in merge) / len(merge) * 1e6, 1)
+        recs.append(rec)
+        rows.append(f"| {label} | `{rec['kernel']}` | {rec['us_per_launch']} | {flops:.4g} | {hw:.4g} | "
+                    f"{hw / flops:.3f} | {100 * util_peak:.1f}% | {100 * util_active:.1f}% | {rec['implied_clock_ghz']} |")
+    out = {"workload": workload, "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"), "launches": recs}
+    lines = [f"# MFMA utilisation of the attention kernel on {workload}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```"] + cmds + ["```", "",
+             "* hw MFMA flops = SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, against the algorithmic flops (4 D per visible "
+             "(query, key) pair and head). The busy-cycle counter gives the same figure: summed over the SIMDs, "
+             "SQ_VALU_MFMA_BUSY_CYCLES x 1024 flops equals the MOPS count.",
+             "* MFMA util at 2.4 GHz = busy cycles per SIMD (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs) / (launch duration "
+             "x 2.4 GHz): the matrix unit's utilisation in the terms of the published peak (the roofline fraction "
+             "of the launch while counters are collected).",
+             "* MFMA busy of active cycles = busy cycles per SIMD / (GRBM_GUI_ACTIVE / 8 XCDs): the same against the "
+             "cycles the GPU actually ran, whatever its clock. GRBM_GUI_ACTIVE also counts some cycles around each "
+             "dispatch, so the implied clock (active cycles / duration) reads high, and the fraction low, on "
+             "launches of tens of microseconds; on launches of hundreds of microseconds and more it shows the "
+             "engine clock under sustained MFMA load.",
+             "* Averages over the probe's launches of each kind, the first (cold) launch of each left out; the "
+             "durations are dispatch timestamps with counters on (a few percent above the bench's event times).",
+             "",
+             "| launch | kernel | us per launch | algorithmic flops | hw MFMA flops | hw / alg | MFMA util at 2.4 GHz | "
+             "MFMA busy of active cycles | implied clock (GHz) |",
+             "|---|---|---|---|---|---|---|---|---|"] + rows
+    if any("merge_kernel_us" in r for r in recs):
+        lines += ["", f"The share's split launch is followed by a merge kernel (`attn_combine_kernel`) of "
+                      f"{recs[-1]['merge_kernel_us']} us per launch (no MFMA work)."]
+    lines += ["", "mfma_json: " + json.dumps(out)]
+    path = os.path.join(ROOT, "profiles", f"attention_mfma_{workload}.md")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
 def _counter_rows(path):
     import csv
     import glob
@@ -192,6 +320,10 @@ def main():
                     help="run only a calibration copy and attention launches (for rocprofv3 --pmc passes)")
     ap.add_argument("--write-traffic-summary", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/attention_traffic_<config>.md from two counter passes")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run only the step and attention launches, all-ranks and one share (for the MFMA counter pass)")
+    ap.add_argument("--write-mfma-summary", metavar="PMC_DIR",
+                    help="write profiles/attention_mfma_<config>.md from one MFMA counter pass")
     ap.add_argument("--write-kernel-trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
                     help="write profiles/kernel_trace_<config>.md from a rocprofv3 --stats run of bench.py")
     ap.add_argument("--profile-command", action="append", default=[],
@@ -205,8 +337,14 @@ def main():
                                    f"rocprofv3 kernel trace: bench step on {args.config}",
                                    "\n".join(args.profile_command), f"kernel_trace_{args.config}.md")
         return
+    if args.write_mfma_summary:
+        write_mfma_summary(args.config, args.write_mfma_summary, args.profile_command)
+        return
     if args.traffic_probe:
         traffic_probe(args.config)
+        return
+    if args.mfma_probe:
+        mfma_probe(args.config)
         return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
