@@ -123,6 +123,54 @@ def test_attention_split_launch_matches_oracle(D, R, B, Tq, Tk, Hl, kv, mask):
     assert err <= TOL["bf16"], err
 
 
+@pytest.mark.parametrize("D,Tq,Tk,Hl,mask", [
+    (128, 1500, 3000, 4, None),       # four query tiles of 24 key tiles per head over 256 CUs
+    (64, 700, 2500, 3, None),
+    (128, 600, 2000, 2, "blocks"),
+])
+def test_attention_split_reused_workspace_and_replays(D, Tq, Tk, Hl, mask):
+    """A split launch depends on nothing left in its workspace: with a
+    workspace full of 0xFF bytes, two launches in a row and three replays of
+    the launch recorded as a HIP graph (other writes to the workspace in
+    between) all give the same bytes, within the oracle's tolerance.  The
+    partial results are merged in a fixed order, so the bytes are the same on
+    every run."""
+    say("attention split reuse", D, Tq, Tk, Hl, mask)
+    rng = np.random.default_rng(Tq + 7 * Tk)
+    m = make_mask(mask, 1, Tq, Tk, rng)
+    q, k, v = (rand_bits(rng, (1, 1, T, Hl, D), "bf16") for T in (Tq, Tk, Tk))
+    need = sp.sp_masked_attention_workspace_size(1, 1, Tq, Tk, Hl, D, sp.SP_BF16, m is not None, 0)
+    plain = 0 if m is None else sp.sp_masked_attention_workspace_size(8, 1, Tq, Tk, 32 * Hl, D, sp.SP_BF16, True, 0)
+    assert need > plain                       # the launch splits
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    qd, kd, vd = to_dev(q), to_dev(k), to_dev(v)
+    md = to_dev(m) if m is not None else None
+    o = sentinel_like((1, 1, Tq, Hl, D), torch.bfloat16)
+    st = lambda T: stacked(1, 1, T, Hl, D)
+    call = lambda: sp.sp_masked_attention(qd, kd, vd, o, 1, 1, Tq, Tk, Hl, D, st(Tq), st(Tk), st(Tk), st(Tq),
+                                          mask=md, workspace=ws)
+    call()
+    torch.cuda.synchronize()
+    first = raw(o)
+    want = O.attention_heads(f64(q[0]), f64(k[0]), f64(v[0]), 1 / math.sqrt(D), Tk, m)
+    assert np.max(np.abs(f64(first) - want)) <= TOL["bf16"]
+    o.view(torch.uint8).fill_(0xFF)
+    call()
+    torch.cuda.synchronize()
+    assert np.array_equal(raw(o), first)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        call()
+    torch.cuda.synchronize()
+    for i in range(3):
+        o.view(torch.uint8).fill_(0xFF)
+        ws[: need // 2].fill_(0xFF)           # eager work on the workspace between replays
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert np.array_equal(raw(o), first), i
+
+
 @pytest.mark.parametrize("D,Tq,Tk,Hl,kv", [
     (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles, ranges of 38 tiles
     (64, 600, 4000, 100, 4000),     # 300 query tiles of 32 key tiles, ranges of 38 (two workgroups per CU)
