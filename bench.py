@@ -535,6 +535,43 @@ def main():
     del sets
     torch.cuda.empty_cache()
 
+    # -- the two gather kernels the same way, back to back over rotating
+    #    buffer sets (the in-step figures above include the gap between
+    #    launches, which weighs more on these 100 MB launches)
+    def rotating_ms(make_set, call, nbytes):
+        n = min(16, max(2, int(math.ceil(1.2e9 / max(nbytes, 1)))))
+        bufs = [make_set() for _ in range(n)]
+        iters = max(args.steps, 2 * n)
+        for i in range(n):
+            call(*bufs[i])
+        torch.cuda.synchronize()
+        t0 = torch.cuda.Event(enable_timing=True)
+        t1 = torch.cuda.Event(enable_timing=True)
+        t0.record(stream)
+        for i in range(iters):
+            call(*bufs[i % n])
+        t1.record(stream)
+        torch.cuda.synchronize()
+        del bufs
+        torch.cuda.empty_cache()
+        return t0.elapsed_time(t1) / iters, n
+
+    def rand_like(t):
+        u = torch.empty_like(t)
+        u.view(torch.uint8).random_()
+        return u
+
+    tq_pad = wl.q_tokens_pad if wl.cross else Tp
+    ms_gh_rot, n_gh = rotating_ms(
+        lambda: (rand_like(step.oh), torch.empty_like(step.ot)),
+        lambda src, dst: binding.sp_relayout_heads([src], [dst], W, B, tq_pad, H, D, binding.SP_HEADS_TO_TOKENS),
+        relayout_o_bytes)
+    ts_q, t_out = tq_pad // W, (wl.Tq if wl.cross else T)
+    ms_gather_rot, n_ga = rotating_ms(
+        lambda: (rand_like(step.ot), torch.empty_like(step.out)),
+        lambda src, dst: binding.sp_gather_unpad(src, dst, W, B, ts_q, H * D, t_out, counts=[ts_q] * W),
+        gather_bytes)
+
     # -- one rank's share alone (R = 1): the attention launch each GPU runs when
     #    the W ranks are devices; few query tiles, so the library splits keys
     share_out = torch.empty_like(step.oh[0])
@@ -593,6 +630,14 @@ def main():
                          "GB/s": round(gbs(relayout_o_bytes, ms_gh), 1)},
         "gather_output_tokens": {"ms": round(ms_gather, 4), "bytes": gather_bytes,
                                  "GB/s": round(gbs(gather_bytes, ms_gather), 1)},
+        "gather_heads_rotating": {"ms": round(ms_gh_rot, 4), "bytes": relayout_o_bytes,
+                                  "GB/s": round(gbs(relayout_o_bytes, ms_gh_rot), 1),
+                                  "hbm_frac": round(gbs(relayout_o_bytes, ms_gh_rot) / PEAK_HBM_GBS, 4),
+                                  "buffer_sets": n_gh},
+        "gather_output_tokens_rotating": {"ms": round(ms_gather_rot, 4), "bytes": gather_bytes,
+                                          "GB/s": round(gbs(gather_bytes, ms_gather_rot), 1),
+                                          "hbm_frac": round(gbs(gather_bytes, ms_gather_rot) / PEAK_HBM_GBS, 4),
+                                          "buffer_sets": n_ga},
         "cp2d_step": cp2d,
         "zero_copy_step": {"ms": round(ms_zero, 4), "TFLOP/s": round(attn_flops / (ms_zero * 1e-3) / 1e12, 2),
                            "output_bytes_equal_to_step": zero_equal},

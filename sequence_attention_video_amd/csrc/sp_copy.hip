@@ -85,6 +85,56 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
   }
 }
 
+// gather_heads walks the token side instead: every workgroup writes whole
+// token rows (the rows of one rank's shard are contiguous), and each 1 KiB
+// wave store is fed by one run of one head-side rank.  Walking the head side
+// here (contiguous reads, stores scattered in runs at the token-row stride)
+// measured 5.0 TB/s on 100 MB against 6.0 for the send direction, whose
+// scattered side is the reads.
+struct GatherHeadsArgs {
+  const char* src[3];
+  char* dst[3];
+  int64_t tok_rank_b, tok_batch_b;    // token side (bytes); rows of W runs packed
+  int64_t head_rank_b, head_batch_b;  // head side (bytes)
+  int64_t run_b;                      // Hl*D*eb
+  int64_t seg_b;                      // Ts*run_b
+  uint32_t V;                         // 16-byte vectors per run
+  FastDiv fdV, fdRow;                 // by V and by W*V (vectors per token row)
+  uint32_t n_per_shard;               // Ts*W*V vectors per (tensor, s, b)
+  uint32_t chunks;                    // workgroups per shard
+};
+
+// blockIdx.x = (token-side rank s, chunk), blockIdx.y = batch b, blockIdx.z =
+// tensor.  Flat vector f of shard (s, b) is token t = f / (W*V), head-group
+// rank r = (f % (W*V)) / V, vector v = f % V of the run; it comes from rank
+// r's head side at token s*Ts + t.
+__global__ __launch_bounds__(kThreads) void gather_heads_kernel(GatherHeadsArgs a) {
+  const uint32_t s = blockIdx.x / a.chunks;
+  const uint32_t chunk = blockIdx.x - s * a.chunks;
+  const int64_t b = blockIdx.y;
+  const int n = blockIdx.z;
+  const char* src = a.src[n] + b * a.head_batch_b + int64_t(s) * a.seg_b;
+  char* dst = a.dst[n] + int64_t(s) * a.tok_rank_b + b * a.tok_batch_b;
+  vec16 buf[kUnroll];
+  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_shard) {
+      const uint32_t t = fdiv(f, a.fdRow);
+      const uint32_t rem = f - t * a.fdRow.d;
+      const uint32_t r = fdiv(rem, a.fdV);
+      const uint32_t v = rem - r * a.V;
+      buf[u] = load16(src + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per_shard) store16(dst + int64_t(f) * 16, buf[u]);
+  }
+}
+
 // ------------------------------------------------------------------ 2-D tiles
 
 struct Tile2dArgs {
@@ -397,6 +447,28 @@ extern "C" sp_status sp_relayout_heads(const void* const* src, void* const* dst,
   const int64_t V = run * eb / 16;
   if (Ts * V >= (int64_t(1) << 32) - kChunk) return SP_ERR_UNSUPPORTED;
   if (int64_t(W) * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  if (dir == SP_HEADS_TO_TOKENS && Ts * V * W < (int64_t(1) << 32) - kChunk &&
+      div_up(Ts * V * W, kChunk) * W < (int64_t(1) << 31)) {
+    GatherHeadsArgs g;
+    for (int i = 0; i < 3; ++i) {
+      g.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);
+      g.dst[i] = static_cast<char*>(dst[i < n_tensors ? i : 0]);
+    }
+    g.tok_rank_b = tok.rank * eb;
+    g.tok_batch_b = tok.batch * eb;
+    g.head_rank_b = head.rank * eb;
+    g.head_batch_b = head.batch * eb;
+    g.run_b = run * eb;
+    g.seg_b = Ts * run * eb;
+    g.V = uint32_t(V);
+    g.fdV = make_fastdiv(uint32_t(V));
+    g.fdRow = make_fastdiv(uint32_t(V * W));
+    g.n_per_shard = uint32_t(Ts * V * W);
+    g.chunks = uint32_t(div_up(Ts * V * W, kChunk));
+    dim3 grid(unsigned(int64_t(g.chunks) * W), unsigned(B), unsigned(n_tensors));
+    hipLaunchKernelGGL(gather_heads_kernel, grid, dim3(kThreads), 0, as_stream(stream), g);
+    return launch_status();
+  }
   RelayoutArgs a;
   for (int i = 0; i < 3; ++i) {
     a.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);

@@ -52,6 +52,28 @@ def test_relayout_bit_exact(W, B, T_pad, H, D, dtype):
     assert raw(tok).tobytes() == O.gather_heads(O.send_recv_heads(O.token_shards(xs[0], W))).tobytes()
     assert raw(tok).tobytes() == O.token_shards(xs[0], W).tobytes()
     assert raw(back).tobytes() == xs[1].tobytes()
+    # all three tensors back in one launch
+    toks = [sentinel_like((W, B, Ts, H, D), TD[dtype]) for _ in range(3)]
+    sp.sp_relayout_heads(heads, toks, W, B, T_pad, H, D, sp.SP_HEADS_TO_TOKENS)
+    torch.cuda.synchronize()
+    for x, t in zip(xs, toks):
+        assert raw(t).tobytes() == O.token_shards(x, W).tobytes()
+
+
+@pytest.mark.parametrize("W,B,T_pad,H,D,dtype", [(4, 2, 64, 8, 64, "bf16"), (2, 3, 30, 4, 16, "f32")])
+def test_gather_heads_strided_head_side(W, B, T_pad, H, D, dtype):
+    """gather_heads from head-side shards that are views into longer buffers
+    (rank and batch strides beyond the packed sizes)."""
+    say("gather_heads strided", W, B, T_pad, H, D, dtype)
+    rng = np.random.default_rng(7 + T_pad)
+    Ts, Hl, extra = T_pad // W, H // W, 5
+    big = rand_bits(rng, (W, B, T_pad + extra, Hl, D), dtype)
+    tok = sentinel_like((W, B, Ts, H, D), TD[dtype])
+    head_view = (B * (T_pad + extra) * Hl * D, (T_pad + extra) * Hl * D)
+    sp.sp_relayout_heads([to_dev(big)], [tok], W, B, T_pad, H, D, sp.SP_HEADS_TO_TOKENS, head_strides=head_view)
+    torch.cuda.synchronize()
+    want = O.gather_heads(np.ascontiguousarray(big[:, :, :T_pad]))
+    assert raw(tok).tobytes() == want.tobytes()
 
 
 def test_relayout_rejects_bad_shapes():
