@@ -286,7 +286,7 @@ def write_kernel_trace_summary(stats_csv: str, bench_json: str, title: str, cmd:
     run) into a short markdown summary under profiles/."""
     import csv
     rows = list(csv.DictReader(open(stats_csv)))
-    bench = json.loads(open(bench_json).read())
+    bench = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith('{"metric"')][-1])
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
              "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
     for r in rows:
@@ -299,8 +299,13 @@ def write_kernel_trace_summary(stats_csv: str, bench_json: str, title: str, cmd:
               f"* masked attention: {k['masked_attention']['ms']*1e3:.1f} us per launch, "
               f"{k['masked_attention']['TFLOP/s']} TFLOP/s ({100*k['masked_attention']['mfma_frac']:.1f}% of the MFMA peak)",
               f"* send_recv_heads (Q, K, V, rotating buffers): {k['send_recv_heads_rotating']['ms']*1e3:.1f} us, "
-              f"{k['send_recv_heads_rotating']['GB/s']} GB/s ({100*k['send_recv_heads_rotating']['hbm_frac']:.1f}% of 8000 GB/s)",
-              f"* kernel source hash: `{bench['kernel_source_hash']}`"]
+              f"{k['send_recv_heads_rotating']['GB/s']} GB/s ({100*k['send_recv_heads_rotating']['hbm_frac']:.1f}% of 8000 GB/s)"]
+    for key, label in (("gather_heads_rotating", "gather_heads (O, rotating buffers)"),
+                       ("gather_output_tokens_rotating", "gather_output_tokens (rotating buffers)")):
+        if key in k:
+            lines.append(f"* {label}: {k[key]['ms']*1e3:.1f} us, {k[key]['GB/s']} GB/s "
+                         f"({100*k[key]['hbm_frac']:.1f}% of 8000 GB/s)")
+    lines.append(f"* kernel source hash: `{bench['kernel_source_hash']}`")
     path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
