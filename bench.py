@@ -447,6 +447,12 @@ def main():
     ms_attn = stage(1, 2)
     ms_gh = stage(2, 3)
     ms_gather = stage(3, 4)
+    per_step = [ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)]
+    per_attn = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
+    spread = {"step_ms_median": round(float(np.median(per_step)), 4), "step_ms_min": round(float(np.min(per_step)), 4),
+              "attention_ms_median": round(float(np.median(per_attn)), 4),
+              "attention_ms_min": round(float(np.min(per_attn)), 4), "steps": args.steps,
+              "note": "per-step event pairs (a second run of K steps with an event between stages)"}
 
     # -- the same step with both exchanges folded into attention's addressing
     #    (one device only: the head-side views are strided views of the
@@ -648,6 +654,7 @@ def main():
                            "output_bytes_equal_to_step": zero_equal},
         "graph_step": {"ms": round(ms_graph, 4), "TFLOP/s": round(attn_flops / (ms_graph * 1e-3) / 1e12, 2),
                        "output_bytes_equal_to_step": graph_equal},
+        "step_spread": spread,
         "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),
                                         "mfma_frac": round(share_tflops / peak_mfma, 4), "R": 1,
                                         "split": share_split,
@@ -656,7 +663,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, x, args.cpu_seconds)
+        cpu = cpu_baseline(wl, x, args.cpu_seconds, step.out.float().cpu().numpy().astype(np.float64))
 
     value = attn_flops / (ms_step * 1e-3) / 1e12
     out = {
@@ -773,9 +780,12 @@ def bench_joint(args):
     print(json.dumps(out), flush=True)
 
 
-def cpu_baseline(wl, x, budget_s: float):
+def cpu_baseline(wl, x, budget_s: float, gpu_out=None):
     """The oracle as it stands, timed on the host on a bounded sample of the same
-    workload: rank 0's local heads, query rows in blocks of 256, all keys."""
+    workload: rank 0's local heads, query rows in blocks of 256, all keys.
+    With gpu_out (the timed step's final output (B, T, H, D) as float64), the
+    sampled oracle rows are also compared with it (outside the timed oracle
+    calls): parity re-checked on the benchmarked buffers."""
     import numpy as np
 
     import oracle as O
@@ -791,6 +801,8 @@ def cpu_baseline(wl, x, budget_s: float):
     flops = 0
     rows_done = 0
     heads_done = []
+    err = 0.0
+    spent = 0.0
     t0 = time.perf_counter()
     for j in range(wl.H):                        # rank 0's heads first, then rank 1's, ...
         kj = widen(O.pad_tokens(x["k"][:, :, j], Tp)[0])
@@ -801,21 +813,31 @@ def cpu_baseline(wl, x, budget_s: float):
         for i0 in range(0, nq, 256):
             i1 = min(nq, i0 + 256)
             mrows = None if mask is None else mask[i0:i1]
-            O.attention(widen(qsrc[i0:i1]), kj, vj, scale, kv_valid, mrows)
+            c0 = time.perf_counter()
+            want = O.attention(widen(qsrc[i0:i1]), kj, vj, scale, kv_valid, mrows)
+            spent += time.perf_counter() - c0
             vis = (i1 - i0) * min(kv_valid, kj.shape[0]) if mrows is None else int(mrows[:, :kv_valid].sum())
             flops += 4 * D * vis
             rows_done += i1 - i0
-            if time.perf_counter() - t0 > budget_s:
+            if gpu_out is not None:
+                keep = min(i1, gpu_out.shape[1]) - i0          # padded query rows are not in the output
+                if keep > 0:
+                    err = max(err, float(np.max(np.abs(gpu_out[0, i0:i0 + keep, j] - want[:keep]))))
+            if spent > budget_s:
                 break
         heads_done.append(j)
-        if time.perf_counter() - t0 > budget_s:
+        if spent > budget_s:
             break
-    dt = time.perf_counter() - t0
-    return {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{rows_done} query rows (batch 0; heads {heads_done[0]}..{heads_done[-1]}, rank-major) "
-                      f"against all {Tp} keys, float64 NumPy oracle, {dt:.1f} s; the whole step is "
-                      f"{wl.H * wl.B} heads of {nq} query rows",
-            "seconds": round(dt, 2)}
+    dt = spent
+    rec = {"value": round(flops / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+           "sample": f"{rows_done} query rows (batch 0; heads {heads_done[0]}..{heads_done[-1]}, rank-major) "
+                     f"against all {Tp} keys, float64 NumPy oracle, {dt:.1f} s; the whole step is "
+                     f"{wl.H * wl.B} heads of {nq} query rows",
+           "seconds": round(dt, 2)}
+    if gpu_out is not None:
+        tol = 2e-2 if wl.dtype == "bf16" else 1e-4
+        rec["timed_output_vs_oracle"] = {"rows": rows_done, "max_abs_err": err, "tol": tol, "ok": err <= tol}
+    return rec
 
 
 if __name__ == "__main__":
