@@ -749,6 +749,20 @@ def bench_joint(args):
     ms_attn_v = float(np.mean([ev[i][n + 1].elapsed_time(ev[i][n + 2]) for i in range(args.steps)]))
     v_tflops = flops["video_self"] / (ms_attn_v * 1e-3) / 1e12
     finite = all(bool(torch.isfinite(o.float()).all().item()) for o in step.run().values())
+    # the same block with the four parts on streams of their own (they share
+    # no buffer); reported beside the sequential step
+    ref = {name: o.clone() for name, o in step.run().items()}
+    for _ in range(max(3, args.warmup // 4)):
+        step.run_concurrent()
+    c0 = torch.cuda.Event(enable_timing=True)
+    c1 = torch.cuda.Event(enable_timing=True)
+    c0.record(stream)
+    for _ in range(args.steps):
+        outs_c = step.run_concurrent()
+    c1.record(stream)
+    torch.cuda.synchronize()
+    ms_conc = c0.elapsed_time(c1) / args.steps
+    conc_equal = all(torch.equal(outs_c[name].view(torch.uint8), ref[name].view(torch.uint8)) for name in names)
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(parts["video_self"], x["video_self"], args.cpu_seconds)
@@ -774,6 +788,8 @@ def bench_joint(args):
         "cpu_baseline": cpu,
         "parts": {n: {"ms": round(part_ms[n], 4), "attention_flops": flops[n],
                       "TFLOP/s_over_path": round(flops[n] / (part_ms[n] * 1e-3) / 1e12, 2)} for n in names},
+        "concurrent_step": {"ms": round(ms_conc, 4), "TFLOP/s": round(total / (ms_conc * 1e-3) / 1e12, 2),
+                            "streams": len(names), "output_bytes_equal_to_step": conc_equal},
         "checks": {"output_finite": finite},
         "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
     }

@@ -6,7 +6,9 @@ multiple of W) at full size on the GPU, against the CPU oracle:
 * every part's final output on sampled query rows (first, last, shard
   boundaries, the last real row) within 2e-2 of unsharded float64 attention
   on the real tokens (the sharded == unsharded invariant);
-* the zero-copy form of every part byte-identical to its exchange path.
+* the zero-copy form of every part byte-identical to its exchange path;
+* the four parts run concurrently on their own streams give the same bytes
+  as run one after another, on several steps in a row.
 """
 
 import math
@@ -69,3 +71,18 @@ def test_joint_av_zero_copy_matches_exchange_path():
         outz = s.run_zero_copy()
         torch.cuda.synchronize()
         assert torch.equal(outz.view(torch.uint8), out.view(torch.uint8)), name
+
+
+def test_joint_av_concurrent_streams_match_sequential():
+    say("joint_av concurrent")
+    jw = JOINT_AV
+    step = JointAVStep(jw, make_joint_inputs(jw))
+    ref = {n: o.clone() for n, o in step.run().items()}
+    torch.cuda.synchronize()
+    for i in range(3):
+        for o in step.run().values():
+            o.view(torch.uint8).fill_(0xFF)       # stale bytes would show
+        outs = step.run_concurrent()
+        torch.cuda.synchronize()
+        for name in JointAVStep.PARTS:
+            assert torch.equal(outs[name].view(torch.uint8), ref[name].view(torch.uint8)), (i, name)
