@@ -498,6 +498,8 @@ def main():
         c0 = torch.cuda.Event(enable_timing=True)
         c1 = torch.cuda.Event(enable_timing=True)
         c2 = torch.cuda.Event(enable_timing=True)
+        c3 = torch.cuda.Event(enable_timing=True)
+        c4 = torch.cuda.Event(enable_timing=True)
         c0.record(stream)
         for _ in range(args.steps):
             step2.run()
@@ -505,14 +507,25 @@ def main():
         for _ in range(args.steps):
             step2.split_cp_2d()
         c2.record(stream)
+        for _ in range(args.steps):
+            step2.split_send_heads()
+        c3.record(stream)
+        for _ in range(args.steps):
+            step2.run_separate()
+        c4.record(stream)
         torch.cuda.synchronize()
         ms_2d = c0.elapsed_time(c1) / args.steps
         ms_tile = c1.elapsed_time(c2) / args.steps
+        ms_fused = c2.elapsed_time(c3) / args.steps
+        ms_sep = c3.elapsed_time(c4) / args.steps
         tile_bytes = 2 * 3 * B * T * H * D * eb
         cp2d = {"ms": round(ms_2d, 4), "TFLOP/s": round(attn_flops / (ms_2d * 1e-3) / 1e12, 2),
                 "split_hw": list(step2.split), "grid_fhw": list(GRIDS[args.config]),
+                "split_send_heads_qkv": {"ms": round(ms_fused, 4), "bytes": tile_bytes,
+                                         "GB/s": round(tile_bytes / (ms_fused * 1e-3) / 1e9, 1)},
                 "split_cp_2d_qkv": {"ms": round(ms_tile, 4), "bytes": tile_bytes,
                                     "GB/s": round(tile_bytes / (ms_tile * 1e-3) / 1e9, 1)},
+                "separate_moves_step_ms": round(ms_sep, 4),
                 "max_abs_diff_vs_step": float((step2.out.float() - step.out.float()).abs().max().item())}
         del step2
 

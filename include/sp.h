@@ -230,6 +230,38 @@ sp_status sp_tile_2d(const void* src, void* dst, int32_t split_h, int32_t split_
                      int64_t height, int64_t width, int64_t C, sp_dtype dtype, sp_tile_dir dir,
                      sp_shard_strides tiles, int64_t grid_batch_stride, void* stream);
 
+/*
+ * sp_tile_2d_relayout_heads -- the 2-D split and the head exchange as one
+ * move ([LC] 智能张量拆分策略: split_tensor_in_cp_2d, then [SP] 换头
+ * send_recv_heads on the tiles; the inverse is [SP] gather_heads, then [LC]
+ * gather_cp_2d).  A bit copy.  W = split_h * split_w ranks, rank s = i*split_w
+ * + j holding tile (i, j) of every frame (th = height/split_h, tw =
+ * width/split_w, Tt = F*th*tw tokens, raster order inside the tile).
+ * grid: (B, T, H, D) tokens in raster order, T = F*height*width, batch b at
+ *   base + b*grid_batch_stride, rows of H*D packed (as in sp_tile_2d).
+ * head side of rank r: (B, T, Hl, D) with Hl = H / W at base + r*head.rank +
+ *   b*head.batch, rows of Hl*D packed; row s*Tt + t holds head group r of rank
+ *   s's tile token t (as sp_relayout_heads leaves it after sp_tile_2d).
+ * SP_TOKENS_TO_HEADS reads the grid (src) and writes the head side (dst): the
+ * same bytes as sp_tile_2d(SP_GRID_TO_TILES) followed by
+ * sp_relayout_heads(SP_TOKENS_TO_HEADS) on stacked tiles (W, B, Tt, H, D);
+ * SP_HEADS_TO_TOKENS is the exact inverse (sp_relayout_heads(
+ * SP_HEADS_TO_TOKENS), then sp_tile_2d(SP_TILES_TO_GRID)).
+ * src, dst: host arrays of n_tensors device pointers (1..3), same shapes and
+ * strides.  Strides in elements.
+ * Errors: height % split_h or width % split_w != 0 -> SP_ERR_NOT_DIVISIBLE;
+ * H % W != 0, n_tensors out of 1..3, negative sizes, split < 1, null,
+ * misaligned (16 bytes) or overlapping pointers, head blocks that overlap,
+ * grid_batch_stride < T*H*D -> SP_ERR_INVALID_ARG; Hl*D*element size not a
+ * multiple of 16 bytes, more than 65535 rank x batch blocks, or an index space
+ * (Tt*Hl*D or T*H*D 16-byte vectors per batch) of 2^32 or more ->
+ * SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_tile_2d_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t split_h,
+                                    int32_t split_w, int64_t B, int64_t F, int64_t height, int64_t width, int32_t H,
+                                    int32_t D, sp_dtype dtype, sp_dir dir, int64_t grid_batch_stride,
+                                    sp_shard_strides head, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

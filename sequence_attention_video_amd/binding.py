@@ -26,7 +26,7 @@ SP_GRID_TO_TILES, SP_TILES_TO_GRID = 0, 1
 EXPORTS = (
     "sp_status_string", "sp_version", "sp_partition", "sp_pad", "sp_relayout_heads",
     "sp_masked_attention_workspace_size", "sp_masked_attention", "sp_gather_unpad", "sp_optimal_split",
-    "sp_tile_2d",
+    "sp_tile_2d", "sp_tile_2d_relayout_heads",
 )
 
 
@@ -77,6 +77,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sp_tile_2d.restype = ctypes.c_int
     lib.sp_tile_2d.argtypes = [vp, vp, i32, i32, i64, i64, i64, i64, i64, ctypes.c_int, ctypes.c_int,
                                ShardStrides, i64, vp]
+    lib.sp_tile_2d_relayout_heads.restype = ctypes.c_int
+    lib.sp_tile_2d_relayout_heads.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i32, i64, i64, i64,
+                                              i64, i32, i32, ctypes.c_int, ctypes.c_int, i64, ShardStrides, vp]
     if path is None:
         _lib = lib
     return lib
@@ -241,3 +244,27 @@ def sp_tile_2d(src, dst, split_h: int, split_w: int, B: int, F: int, height: int
     check(load().sp_tile_2d(_ptr(src), _ptr(dst), int(split_h), int(split_w), int(B), int(F), int(height),
                             int(width), int(C), _dtype_code(grid), int(direction), ShardStrides(*ts), int(gbs),
                             _stream(stream)))
+
+
+def sp_tile_2d_relayout_heads(src, dst, split_h: int, split_w: int, B: int, F: int, height: int, width: int,
+                              H: int, D: int, direction: int, grid_batch_stride=None, head_strides=None,
+                              stream=None):
+    """split_cp_2d + send_recv_heads (SP_TOKENS_TO_HEADS: grid -> head side) or
+    gather_heads + gather_cp_2d (SP_HEADS_TO_TOKENS: head side -> grid) as one
+    move.  ``src``/``dst``: lists of 1..3 tensors.  Default layouts: grid
+    (B, F*height*width, H, D), head side stacked (W, B, T, Hl, D)."""
+    src, dst = list(src), list(dst)
+    _cuda(*src, *dst)
+    if len(dst) != len(src):
+        raise ValueError("one destination per source")
+    W = int(split_h) * int(split_w)
+    T = F * height * width
+    Hl = H // max(W, 1)
+    gbs = grid_batch_stride if grid_batch_stride is not None else T * H * D
+    head = head_strides or (B * T * Hl * D, T * Hl * D)
+    n = len(src)
+    sp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in src])
+    dp = (ctypes.c_void_p * max(n, 1))(*[t.data_ptr() for t in dst])
+    check(load().sp_tile_2d_relayout_heads(sp, dp, n, int(split_h), int(split_w), int(B), int(F), int(height),
+                                           int(width), int(H), int(D), _dtype_code(src[0]), int(direction), int(gbs),
+                                           ShardStrides(*head), _stream(stream)))

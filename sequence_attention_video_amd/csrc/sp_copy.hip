@@ -187,6 +187,104 @@ __global__ __launch_bounds__(kThreads) void tile_2d_kernel(Tile2dArgs a) {
   }
 }
 
+// ------------------------------------------------------------------ 2-D split + head exchange
+
+// The 2-D split (split_cp_2d) followed by the head exchange (send_recv_heads)
+// is one permutation of token rows and head groups, and so is its inverse:
+// rank r's head side holds, at row s*Tt + t, head group r of grid token
+// g(s, t) = (fr*height + i*th + y)*width + j*tw + x, where rank s = i*split_w
+// + j and its tile token t = (fr*th + y)*tw + x.  Moving the bytes once per
+// direction skips the tile-side copy.  Both kernels walk their destination
+// contiguously (1 KiB wave stores; sources in whole runs).
+struct Tile2dHeadsArgs {
+  const char* src[3];
+  char* dst[3];
+  int64_t B;
+  int64_t grid_batch_b, grid_row_b;   // grid side (bytes); rows of W runs packed
+  int64_t head_rank_b, head_batch_b;  // head side (bytes)
+  int64_t run_b;                      // Hl*D*eb
+  int64_t height, width, th, tw, Tt;  // grid and tile sizes (tokens)
+  int32_t split_w;
+  uint32_t V;                         // 16-byte vectors per run
+  FastDiv fdV, fd_tw, fd_th;          // to heads: t -> (fr, y, x)
+  FastDiv fd_row, fd_width, fd_height;  // to grid: f -> grid token -> (fr, y_, x_)
+  uint32_t n_per;                     // vectors per workgroup-row of the grid: Tt*V or T*W*V
+  uint32_t chunks;
+};
+
+// blockIdx.x = (source rank s, chunk), blockIdx.y = (head-group rank r, batch
+// b), blockIdx.z = tensor.  Flat vector f of the head-side segment (r, b, s)
+// is tile token t = f / V, vector f % V of its run.
+__global__ __launch_bounds__(kThreads) void tile_2d_to_heads_kernel(Tile2dHeadsArgs a) {
+  const uint32_t s = blockIdx.x / a.chunks;
+  const uint32_t chunk = blockIdx.x - s * a.chunks;
+  const int64_t r = blockIdx.y / a.B;
+  const int64_t b = blockIdx.y - r * a.B;
+  const int n = blockIdx.z;
+  const int64_t i = s / uint32_t(a.split_w), j = s - (s / uint32_t(a.split_w)) * uint32_t(a.split_w);
+  const char* src = a.src[n] + b * a.grid_batch_b + r * a.run_b;
+  char* dst = a.dst[n] + r * a.head_rank_b + b * a.head_batch_b + int64_t(s) * a.Tt * a.run_b;
+  const int64_t row0 = i * a.th * a.width + j * a.tw;   // grid token of the tile's first token
+  vec16 buf[kUnroll];
+  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per) {
+      const uint32_t t = fdiv(f, a.fdV);
+      const uint32_t v = f - t * a.V;
+      const uint32_t q = fdiv(t, a.fd_tw);
+      const uint32_t x = t - q * uint32_t(a.tw);
+      const uint32_t fr = fdiv(q, a.fd_th);
+      const uint32_t y = q - fr * uint32_t(a.th);
+      const int64_t g = row0 + (int64_t(fr) * a.height + y) * a.width + x;
+      buf[u] = load16(src + g * a.grid_row_b + int64_t(v) * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per) store16(dst + int64_t(f) * 16, buf[u]);
+  }
+}
+
+// blockIdx.x = chunk, blockIdx.y = batch b, blockIdx.z = tensor.  Flat
+// vector f of batch b's grid is grid token g = f / (W*V), head-group rank
+// r = (f % (W*V)) / V, vector f % V of the run; it comes from rank r's head
+// side at the row of g's tile token.
+__global__ __launch_bounds__(kThreads) void tile_2d_from_heads_kernel(Tile2dHeadsArgs a) {
+  const int64_t b = blockIdx.y;
+  const int n = blockIdx.z;
+  const char* src = a.src[n] + b * a.head_batch_b;
+  char* dst = a.dst[n] + b * a.grid_batch_b;
+  vec16 buf[kUnroll];
+  const uint32_t f0 = blockIdx.x * uint32_t(kChunk) + threadIdx.x;
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per) {
+      const uint32_t g = fdiv(f, a.fd_row);
+      const uint32_t rem = f - g * a.fd_row.d;
+      const uint32_t r = fdiv(rem, a.fdV);
+      const uint32_t v = rem - r * a.V;
+      const uint32_t q = fdiv(g, a.fd_width);
+      const uint32_t x_ = g - q * uint32_t(a.width);
+      const uint32_t fr = fdiv(q, a.fd_height);
+      const uint32_t y_ = q - fr * uint32_t(a.height);
+      const uint32_t i = fdiv(y_, a.fd_th), j = fdiv(x_, a.fd_tw);
+      const uint32_t y = y_ - i * uint32_t(a.th), x = x_ - j * uint32_t(a.tw);
+      const int64_t s = int64_t(i) * a.split_w + j;
+      const int64_t t = (int64_t(fr) * a.th + y) * a.tw + x;
+      buf[u] = load16(src + int64_t(r) * a.head_rank_b + (s * a.Tt + t) * a.run_b + int64_t(v) * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < a.n_per) store16(dst + int64_t(f) * 16, buf[u]);
+  }
+}
+
 // ------------------------------------------------------------------ pad
 
 struct PadArgs {
@@ -587,5 +685,81 @@ extern "C" sp_status sp_tile_2d(const void* src, void* dst, int32_t split_h, int
   a.chunks = uint32_t(div_up(n_per_rb, kChunk));
   a.to_tiles = dir == SP_GRID_TO_TILES;
   hipLaunchKernelGGL(tile_2d_kernel, dim3(a.chunks, unsigned(N * B)), dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" sp_status sp_tile_2d_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors,
+                                               int32_t split_h, int32_t split_w, int64_t B, int64_t F,
+                                               int64_t height, int64_t width, int32_t H, int32_t D, sp_dtype dtype,
+                                               sp_dir dir, int64_t grid_batch_stride, sp_shard_strides head,
+                                               void* stream) {
+  if (!dtype_ok(dtype) || (dir != SP_TOKENS_TO_HEADS && dir != SP_HEADS_TO_TOKENS)) return SP_ERR_INVALID_ARG;
+  if (split_h < 1 || split_w < 1 || B < 0 || F < 0 || height < 0 || width < 0 || H < 1 || D < 1)
+    return SP_ERR_INVALID_ARG;
+  if (height % split_h != 0 || width % split_w != 0) return SP_ERR_NOT_DIVISIBLE;
+  const int64_t W = int64_t(split_h) * split_w;
+  if (H % W != 0) return SP_ERR_INVALID_ARG;
+  if (n_tensors < 1 || n_tensors > 3 || src == nullptr || dst == nullptr) return SP_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t Hl = H / W, run = Hl * D;
+  if ((run * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  const int64_t th = height / split_h, tw = width / split_w;
+  const int64_t T = F * height * width, Tt = F * th * tw;
+  if (grid_batch_stride < T * H * D || (grid_batch_stride * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  if (((head.rank | head.batch) * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  if (!disjoint_blocks(head.rank, head.batch, W, B, T * run)) return SP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (src[i] == nullptr || dst[i] == nullptr || !aligned16(src[i]) || !aligned16(dst[i])) return SP_ERR_INVALID_ARG;
+  }
+  const int64_t grid_span = B > 0 ? ((B - 1) * grid_batch_stride + T * H * D) * eb : 0;
+  const int64_t head_span = B > 0 ? ((W - 1) * head.rank + (B - 1) * head.batch + T * run) * eb : 0;
+  const int64_t s_span = dir == SP_TOKENS_TO_HEADS ? grid_span : head_span;
+  const int64_t d_span = dir == SP_TOKENS_TO_HEADS ? head_span : grid_span;
+  // no destination may overlap any source or another destination
+  for (int i = 0; i < n_tensors && B > 0 && T > 0; ++i) {
+    const char* d0 = static_cast<const char*>(dst[i]);
+    for (int j = 0; j < n_tensors; ++j) {
+      const char* s0 = static_cast<const char*>(src[j]);
+      if (s0 < d0 + d_span && d0 < s0 + s_span) return SP_ERR_INVALID_ARG;
+      const char* d1 = static_cast<const char*>(dst[j]);
+      if (j != i && d1 < d0 + d_span && d0 < d1 + d_span) return SP_ERR_INVALID_ARG;
+    }
+  }
+  if (B == 0 || T == 0) return SP_OK;
+  const int64_t V = run * eb / 16;
+  const int64_t n_per = dir == SP_TOKENS_TO_HEADS ? Tt * V : T * W * V;
+  if (n_per >= (int64_t(1) << 32) - kChunk || T >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  if (W * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  Tile2dHeadsArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);
+    a.dst[i] = static_cast<char*>(dst[i < n_tensors ? i : 0]);
+  }
+  a.B = B;
+  a.grid_batch_b = grid_batch_stride * eb;
+  a.grid_row_b = int64_t(H) * D * eb;
+  a.head_rank_b = head.rank * eb;
+  a.head_batch_b = head.batch * eb;
+  a.run_b = run * eb;
+  a.height = height; a.width = width; a.th = th; a.tw = tw; a.Tt = Tt;
+  a.split_w = split_w;
+  a.V = uint32_t(V);
+  a.fdV = make_fastdiv(uint32_t(V));
+  a.fd_tw = make_fastdiv(uint32_t(tw));
+  a.fd_th = make_fastdiv(uint32_t(th));
+  a.fd_row = make_fastdiv(uint32_t(W * V));
+  a.fd_width = make_fastdiv(uint32_t(width));
+  a.fd_height = make_fastdiv(uint32_t(height));
+  a.n_per = uint32_t(n_per);
+  a.chunks = uint32_t(div_up(n_per, kChunk));
+  if (dir == SP_TOKENS_TO_HEADS) {
+    const int64_t gx = int64_t(a.chunks) * W;
+    if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(tile_2d_to_heads_kernel, dim3(unsigned(gx), unsigned(W * B), unsigned(n_tensors)),
+                       dim3(kThreads), 0, as_stream(stream), a);
+  } else {
+    hipLaunchKernelGGL(tile_2d_from_heads_kernel, dim3(a.chunks, unsigned(B), unsigned(n_tensors)), dim3(kThreads),
+                       0, as_stream(stream), a);
+  }
   return launch_status();
 }

@@ -297,6 +297,8 @@ class Ulysses2DStep:
     shards, and gather_cp_2d (sp_tile_2d) restores raster order.  Attention
     does not depend on token order (key-only mask, no padding: the grid must
     split evenly), so the output is the same attention up to summation order.
+    run() does each split and exchange pair as one move; run_separate() keeps
+    them apart (same bytes).
     Memory: tiles (W, B, Tt, H, D) with Tt = F*th*tw; head side
     (W, B, T, Hl, D) in rank-then-tile token order."""
 
@@ -346,7 +348,30 @@ class Ulysses2DStep:
         F, Hh, Ww = self.grid
         sp.sp_tile_2d(self.ot, self.out, *self.split, wl.B, F, Hh, Ww, wl.H * wl.D, sp.SP_TILES_TO_GRID)
 
+    # On one device the split and the exchange are one permutation each way
+    # (sp_tile_2d_relayout_heads): the grid goes straight to the head side
+    # and back, with the same bytes as the two separate moves.
+    def split_send_heads(self):
+        wl = self.wl
+        F, Hh, Ww = self.grid
+        sp.sp_tile_2d_relayout_heads([self.q, self.k, self.v], [self.qh, self.kh, self.vh], *self.split, wl.B, F,
+                                     Hh, Ww, wl.H, wl.D, sp.SP_TOKENS_TO_HEADS)
+
+    def gather_heads_cp_2d(self):
+        wl = self.wl
+        F, Hh, Ww = self.grid
+        sp.sp_tile_2d_relayout_heads([self.oh], [self.out], *self.split, wl.B, F, Hh, Ww, wl.H, wl.D,
+                                     sp.SP_HEADS_TO_TOKENS)
+
     def run(self):
+        self.split_send_heads()
+        self.attention()
+        self.gather_heads_cp_2d()
+        return self.out
+
+    def run_separate(self):
+        """The same step with the split and the exchange as separate moves
+        (split_cp_2d, send_recv_heads; gather_heads, gather_cp_2d)."""
         self.split_cp_2d()
         self.send_recv_heads()
         self.attention()

@@ -306,3 +306,41 @@ def test_tile_2d_validation(lib):
     # nothing to copy is a no-op
     assert lib.sp_tile_2d(None, None, 2, 4, 0, 16, 16, 24, C, b.SP_BF16, b.SP_GRID_TO_TILES, st, 6144 * C,
                           None) == b.SP_OK
+
+
+def test_tile_2d_relayout_heads_validation(lib):
+    """Argument checks of the fused 2-D split + head exchange (host only: every
+    call here is rejected, or has nothing to move, before any launch)."""
+    from sequence_attention_video_amd import binding as b
+    S = b.ShardStrides
+    vp = ctypes.c_void_p
+    src = (vp * 3)(vp(1 << 40), vp((1 << 40) + (1 << 32)), vp((1 << 40) + (2 << 32)))
+    dst = (vp * 3)(vp(1 << 41), vp((1 << 41) + (1 << 32)), vp((1 << 41) + (2 << 32)))
+    H, D, T = 32, 128, 6144
+    hs = S(T * 4 * D, T * 4 * D)
+    call = lambda *a: lib.sp_tile_2d_relayout_heads(*a)
+    # 16 x 24 does not split into 3 x 4 rank rows; H not divisible by the 8 ranks
+    assert call(src, dst, 3, 3, 4, 1, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D, hs,
+                None) == b.SP_ERR_NOT_DIVISIBLE
+    assert call(src, dst, 3, 2, 4, 1, 16, 16, 24, 12, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * 12 * D, hs,
+                None) == b.SP_ERR_INVALID_ARG
+    # bad tensor count, bad direction, null array, grid batch stride too small
+    assert call(src, dst, 4, 2, 4, 1, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D, hs,
+                None) == b.SP_ERR_INVALID_ARG
+    assert call(src, dst, 3, 2, 4, 1, 16, 16, 24, H, D, b.SP_BF16, 5, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    assert call(None, dst, 3, 2, 4, 1, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D, hs,
+                None) == b.SP_ERR_INVALID_ARG
+    assert call(src, dst, 3, 2, 4, 1, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D - 8, hs,
+                None) == b.SP_ERR_INVALID_ARG
+    # a destination overlapping a source; head blocks that overlap each other
+    dst_bad = (vp * 3)(vp((1 << 40) + 4096), dst[1], dst[2])
+    assert call(src, dst_bad, 3, 2, 4, 1, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D, hs,
+                None) == b.SP_ERR_INVALID_ARG
+    assert call(src, dst, 3, 2, 4, 2, 16, 16, 24, H, D, b.SP_BF16, b.SP_TOKENS_TO_HEADS, T * H * D,
+                S(T * 4 * D, 100), None) == b.SP_ERR_INVALID_ARG
+    # a head group of 2 x 1 fp32 values is not a whole 16-byte vector
+    assert call(src, dst, 1, 2, 4, 1, 16, 16, 24, 16, 1, b.SP_F32, b.SP_TOKENS_TO_HEADS, T * 16, S(T * 2, T * 2),
+                None) == b.SP_ERR_UNSUPPORTED
+    # nothing to move is a no-op
+    assert call(src, dst, 3, 2, 4, 0, 16, 16, 24, H, D, b.SP_BF16, b.SP_HEADS_TO_TOKENS, T * H * D, hs,
+                None) == b.SP_OK

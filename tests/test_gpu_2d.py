@@ -2,9 +2,13 @@
 
 * sp_tile_2d, both directions: bit-exact against split_cp_2d / gather_cp_2d
   (small ragged grids and the full video grid), and the round trip;
+* sp_tile_2d_relayout_heads, both directions: bit-exact against the oracle's
+  send_recv_heads(split_cp_2d(x)) and gather_cp_2d(gather_heads(o)), one to
+  three tensors per launch, stacked and strided head sides;
 * the whole 2-D path (Ulysses2DStep) on the workloads that are one video
   grid: sampled query rows within 2e-2 of unsharded float64 attention, and
-  the output within a bf16 rounding step of the 1-D path's.
+  the output within a bf16 rounding step of the 1-D path's, and the same
+  bytes with the split and exchange fused or separate.
 """
 
 import math
@@ -72,3 +76,82 @@ def test_2d_path_matches_oracle_and_1d_path(name):
     q64 = f64(x["q"])[:, rows]
     want = O.attention_heads(q64, f64(x["k"]), f64(x["v"]), 1.0 / math.sqrt(wl.D), wl.T, None)
     assert np.max(np.abs(got[:, rows] - want)) <= 2e-2
+
+
+FUSED_CASES = [
+    # B, F, height, width, n_ranks, H, D, dtype, tensors
+    (2, 3, 6, 4, 6, 12, 16, "f32", 1),     # 3 x 2 ranks, runs of 2 x 16 fp32
+    (1, 2, 4, 6, 4, 8, 64, "bf16", 3),     # 2 x 2 ranks, Q/K/V in one launch
+    (3, 1, 8, 8, 8, 16, 64, "bf16", 2),
+    (1, 3, 9, 6, 3, 6, 32, "bf16", 1),     # odd rank count: 3 x 1
+    (1, 16, 16, 24, 8, 32, 128, "bf16", 3),   # the video grid, Q/K/V
+]
+
+
+def _bits(rng, shape, dtype):
+    host = rng.integers(0, 1 << 16, size=shape).astype(np.uint16 if dtype == "bf16" else np.uint32)
+    t = torch.from_numpy(host.view(np.int16) if dtype == "bf16" else host.view(np.float32)).cuda()
+    return host, (t.view(torch.bfloat16) if dtype == "bf16" else t)
+
+
+@pytest.mark.parametrize("B,F,Hh,Ww,n,H,D,dtype,nt", FUSED_CASES)
+def test_tile_2d_relayout_heads_bit_exact(B, F, Hh, Ww, n, H, D, dtype, nt):
+    say("tile_2d_relayout_heads", B, F, Hh, Ww, n, H, D, dtype, nt)
+    sh, sw = sp.sp_optimal_split(n, Hh, Ww)
+    T, Hl = F * Hh * Ww, H // n
+    rng = np.random.default_rng(T + H + D)
+    xs = [_bits(rng, (B, T, H, D), dtype) for _ in range(nt)]
+    heads = [torch.empty((n, B, T, Hl, D), dtype=xs[0][1].dtype, device="cuda") for _ in range(nt)]
+    for h in heads:
+        h.view(torch.uint8).fill_(0xFF)
+    sp.sp_tile_2d_relayout_heads([x for _, x in xs], heads, sh, sw, B, F, Hh, Ww, H, D, sp.SP_TOKENS_TO_HEADS)
+    backs = [torch.empty_like(x) for _, x in xs]
+    for t in backs:
+        t.view(torch.uint8).fill_(0xFF)
+    sp.sp_tile_2d_relayout_heads(heads, backs, sh, sw, B, F, Hh, Ww, H, D, sp.SP_HEADS_TO_TOKENS)
+    torch.cuda.synchronize()
+    for (host, _), h, back in zip(xs, heads, backs):
+        want = O.send_recv_heads(O.split_cp_2d(host.reshape(B, T, H, D), F, Hh, Ww, sh, sw))
+        assert raw(h).tobytes() == want.tobytes()
+        assert O.gather_cp_2d(O.gather_heads(want), F, Hh, Ww, sh, sw).tobytes() == host.tobytes()
+        assert raw(back).tobytes() == host.tobytes()
+
+
+def test_tile_2d_relayout_heads_strided():
+    """Head-side shards inside longer buffers and a padded grid batch stride."""
+    say("tile_2d_relayout_heads strided")
+    B, F, Hh, Ww, n, H, D = 2, 2, 4, 6, 4, 8, 64
+    sh, sw = sp.sp_optimal_split(n, Hh, Ww)
+    T, Hl, extra = F * Hh * Ww, H // n, 3
+    rng = np.random.default_rng(11)
+    host, _ = _bits(rng, (B, T + extra, H, D), "bf16")
+    x = torch.from_numpy(host.view(np.int16)).cuda().view(torch.bfloat16)
+    big = torch.empty((n, B, T + extra, Hl, D), dtype=torch.bfloat16, device="cuda")
+    big.view(torch.uint8).fill_(0xFF)
+    hs = (B * (T + extra) * Hl * D, (T + extra) * Hl * D)
+    sp.sp_tile_2d_relayout_heads([x], [big], sh, sw, B, F, Hh, Ww, H, D, sp.SP_TOKENS_TO_HEADS,
+                                 grid_batch_stride=(T + extra) * H * D, head_strides=hs)
+    back = torch.empty((B, T + extra, H, D), dtype=torch.bfloat16, device="cuda")
+    back.view(torch.uint8).fill_(0xFF)
+    sp.sp_tile_2d_relayout_heads([big], [back], sh, sw, B, F, Hh, Ww, H, D, sp.SP_HEADS_TO_TOKENS,
+                                 grid_batch_stride=(T + extra) * H * D, head_strides=hs)
+    torch.cuda.synchronize()
+    want = O.send_recv_heads(O.split_cp_2d(np.ascontiguousarray(host[:, :T]), F, Hh, Ww, sh, sw))
+    got = raw(big)
+    assert got[:, :, :T].tobytes() == want.tobytes()
+    assert (got[:, :, T:] == 0xFFFF).all()                  # rows past T untouched
+    assert raw(back)[:, :T].tobytes() == host[:, :T].tobytes()
+    assert (raw(back)[:, T:] == 0xFFFF).all()
+
+
+@pytest.mark.parametrize("name", sorted(GRIDS))
+def test_2d_path_fused_equals_separate(name):
+    wl = WORKLOADS[name]
+    say("2d path fused vs separate", name)
+    x = make_inputs(wl)
+    step2 = Ulysses2DStep(wl, GRIDS[name], to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]))
+    fused = step2.run().clone()
+    step2.out.view(torch.uint8).fill_(0xFF)
+    sep = step2.run_separate()
+    torch.cuda.synchronize()
+    assert torch.equal(fused.view(torch.uint8), sep.view(torch.uint8))
