@@ -78,9 +78,15 @@ class UlyssesStep:
                 self.mask_ext = torch.empty(mask.shape[0], Tp, Tp, dtype=torch.uint8, device=device)
             else:
                 self.mask_ext = mask          # already (B, T_pad, T_pad): extension is the identity
-            need = sp.sp_masked_attention_workspace_size(W, B, Tp, Tp, Hl, D, sp._dtype_code(self.qh), True,
-                                                         Tp * Tp if mask.shape[0] > 1 else 0)
-            self.workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device)
+        # the all-ranks attention launch's workspace (mask classes, or the
+        # partial records of a split launch), allocated once: run() allocates
+        # nothing
+        tq_attn = wl.q_tokens_pad if wl.cross else Tp
+        need = sp.sp_masked_attention_workspace_size(W, B, tq_attn, Tp, Hl, D, sp._dtype_code(self.kh),
+                                                     mask is not None,
+                                                     Tp * Tp if mask is not None and mask.shape[0] > 1 else 0)
+        if need:
+            self.workspace = torch.empty(need, dtype=torch.uint8, device=device)
         self.scale = 1.0 / math.sqrt(D)
 
     # -- the step's stages, each one library call (or one host call) ----------
@@ -121,7 +127,8 @@ class UlyssesStep:
             qs = (Hl * D, Tq * H * D, H * D, D)            # rank r's heads of the unexchanged Q
             os_ = (B * Tq * Hl * D, Tq * Hl * D, Hl * D, D)
             sp.sp_masked_attention(self.qc, self.kh, self.vh, self.oh, wl.W, B, Tq, Tp, Hl, D,
-                                   qs, head_side, head_side, os_, kv_valid_len=wl.T, scale=self.scale)
+                                   qs, head_side, head_side, os_, kv_valid_len=wl.T, scale=self.scale,
+                                   workspace=self.workspace)
             return
         if self.mask is not None:
             sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, Tp, Tp, Hl, D,
@@ -130,7 +137,7 @@ class UlyssesStep:
         else:
             sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, Tp, Tp, Hl, D,
                                    head_side, head_side, head_side, head_side, kv_valid_len=wl.T,
-                                   scale=self.scale)
+                                   scale=self.scale, workspace=self.workspace)
 
     def attention_rank(self, r: int, out, workspace=None):
         """Rank r's share alone (R = 1): the attention launch one GPU runs when
@@ -213,13 +220,13 @@ class UlyssesStep:
             Tq = wl.q_tokens_pad
             qo = (Hl * D, Tq * H * D, H * D, D)
             sp.sp_masked_attention(self.qc, self.kp, self.vp, self.oz, wl.W, B, Tq, Tp, Hl, D, qo, tok, tok, qo,
-                                   kv_valid_len=wl.T, scale=self.scale)
+                                   kv_valid_len=wl.T, scale=self.scale, workspace=self.workspace)
         elif self.mask is not None:
             sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
                                    kv_valid_len=Tp, mask=self.mask_ext, scale=self.scale, workspace=self.workspace)
         else:
             sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
-                                   kv_valid_len=wl.T, scale=self.scale)
+                                   kv_valid_len=wl.T, scale=self.scale, workspace=self.workspace)
 
     def gather_output_tokens_z(self, lengths):
         wl = self.wl
@@ -319,6 +326,8 @@ class Ulysses2DStep:
         self.oh = e(W, B, T, Hl, D)
         self.ot = e(W, B, self.Tt, H, D)
         self.out = e(B, T, H, D)
+        need = sp.sp_masked_attention_workspace_size(W, B, T, T, Hl, D, sp._dtype_code(self.qh), False, 0)
+        self.workspace = torch.empty(need, dtype=torch.uint8, device=device) if need else None
         self.scale = 1.0 / math.sqrt(D)
 
     def split_cp_2d(self):
@@ -337,7 +346,7 @@ class Ulysses2DStep:
         B, T, Hl, D = wl.B, wl.T, wl.Hl, wl.D
         hs = (B * T * Hl * D, T * Hl * D, Hl * D, D)
         sp.sp_masked_attention(self.qh, self.kh, self.vh, self.oh, wl.W, B, T, T, Hl, D, hs, hs, hs, hs,
-                               kv_valid_len=T, scale=self.scale)
+                               kv_valid_len=T, scale=self.scale, workspace=self.workspace)
 
     def gather_heads(self):
         wl = self.wl

@@ -193,3 +193,49 @@ def test_workload_step_graph_replays(name):
         g.replay()
         torch.cuda.synchronize()
         assert torch.equal(step.out.view(torch.uint8), want.view(torch.uint8)), i
+
+
+def _allocations():
+    return torch.cuda.memory_stats().get("allocation.all.allocated", 0)
+
+
+@pytest.mark.parametrize("name", ORDER)
+def test_workload_step_allocates_nothing(name):
+    """Buffers and workspaces are made when the step is built: run() and
+    run_zero_copy() make no device allocation (so a captured graph or a
+    serving loop reuses the same memory every step)."""
+    wl = WORKLOADS[name]
+    say("step allocations", name)
+    x = make_inputs(wl)
+    q, k, v = to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"])
+    mask = to_dev(x["mask"]) if x["mask"] is not None else None
+    step = UlyssesStep(wl, q, k, v, mask)
+    step.run()
+    step.run_zero_copy()                   # its buffers are made on first use
+    torch.cuda.synchronize()
+    before = _allocations()
+    for _ in range(2):
+        step.run()
+        step.run_zero_copy()
+    torch.cuda.synchronize()
+    assert _allocations() == before
+
+
+def test_joint_and_2d_steps_allocate_nothing():
+    from sequence_attention_video_amd.pipeline import JointAVStep, Ulysses2DStep
+    from sequence_attention_video_amd.workloads import GRIDS, JOINT_AV, make_joint_inputs
+    say("step allocations joint_av and 2-D")
+    joint = JointAVStep(JOINT_AV, make_joint_inputs(JOINT_AV))
+    joint.run()
+    joint.run_concurrent()
+    wl = WORKLOADS["video_self"]
+    x = make_inputs(wl)
+    step2 = Ulysses2DStep(wl, GRIDS["video_self"], to_dev(x["q"]), to_dev(x["k"]), to_dev(x["v"]))
+    step2.run()
+    torch.cuda.synchronize()
+    before = _allocations()
+    joint.run()
+    joint.run_concurrent()
+    step2.run()
+    torch.cuda.synchronize()
+    assert _allocations() == before
