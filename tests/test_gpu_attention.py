@@ -171,6 +171,36 @@ def test_attention_split_reused_workspace_and_replays(D, Tq, Tk, Hl, mask):
         assert np.array_equal(raw(o), first), i
 
 
+@pytest.mark.parametrize("D,Tq,Tk,Hl,blank", [
+    (128, 1000, 2000, 2, "tile"),     # query tile 1 (rows 384..767) sees no key: an item with no work
+    (64, 700, 2500, 3, "tile"),
+    (128, 1000, 2000, 2, "all"),      # nothing visible anywhere: no range has a unit
+    (128, 600, 3000, 3, "ends"),      # only the first and the last key tiles visible
+])
+def test_attention_masked_split_uneven_work(D, Tq, Tk, Hl, blank):
+    """Masked split launches over very uneven work: a query tile with no
+    visible key, a mask with nothing visible, visible keys only at both ends.
+    Every row is written once, rows that see nothing are 0."""
+    say("attention masked split uneven", D, Tq, Tk, Hl, blank)
+    rng = np.random.default_rng(Tq + Tk + Hl)
+    m = (rng.random((1, Tq, Tk)) < 0.6).astype(np.uint8)
+    BM = 384 if D == 128 else 256
+    if blank == "tile":
+        m[0, BM:2 * BM] = 0
+    elif blank == "all":
+        m[:] = 0
+    else:
+        m[0, :, 128:Tk - 128] = 0
+    need = sp.sp_masked_attention_workspace_size(1, 1, Tq, Tk, Hl, D, sp.SP_BF16, True, 0)
+    plain = sp.sp_masked_attention_workspace_size(8, 1, Tq, Tk, 32 * Hl, D, sp.SP_BF16, True, 0)
+    assert need > plain                      # the launch splits
+    got, want = run_case("bf16", D, 1, 1, Tq, Tk, Hl, Tk, m, seed=Tq + D)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+    if blank == "all":
+        assert not got.any()
+
+
 @pytest.mark.parametrize("D,Tq,Tk,Hl,kv", [
     (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles, ranges of 38 tiles
     (64, 600, 4000, 100, 4000),     # 300 query tiles of 32 key tiles, ranges of 38 (two workgroups per CU)
