@@ -255,12 +255,13 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
             kname[r["Dispatch_Id"]] = r["Kernel_Name"]
         copy = [per[i] for i in per if "copy" in kname[i].lower() and "attn" not in kname[i]]
         attn = [per[i] for i in per if "attn_bf16_kernel" in kname[i] or "attn_f32_kernel" in kname[i]]
-        relay = [per[i] for i in per if "relayout_kernel" in kname[i]]
         copy_kib = max(copy) if copy else float("nan")
         scale = (COPY_PROBE_BYTES / 1024.0) / copy_kib        # true KiB per counted KiB
+        first = lambda key: next((per[i] for i in sorted(per, key=int) if key in kname[i]), float("nan"))
         out[name] = {"copy_kib": copy_kib, "scale": scale,
                      "attention_kib": sum(attn[1:]) / max(1, len(attn[1:])) if len(attn) > 1 else (attn[0] if attn else float("nan")),
-                     "relayout_kib": relay[0] if relay else float("nan")}
+                     "send_kib": first("relayout_kernel"), "gather_heads_kib": first("gather_heads_kernel"),
+                     "gather_unpad_kib": first("gather_unpad_kernel")}
     fetch_b = out["FETCH_SIZE"]["attention_kib"] * out["FETCH_SIZE"]["scale"] * 1024
     write_b = out["WRITE_SIZE"]["attention_kib"] * out["WRITE_SIZE"]["scale"] * 1024
     rec = {"workload": workload, "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
@@ -274,8 +275,28 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
              f"{out['FETCH_SIZE']['scale']:.3f} and {out['WRITE_SIZE']['scale']:.3f}.", "",
              "| counter | attention, KiB per launch (raw) | scaled bytes per launch |", "|---|---|---|",
              f"| FETCH_SIZE | {out['FETCH_SIZE']['attention_kib']:.0f} | {fetch_b:.4g} |",
-             f"| WRITE_SIZE | {out['WRITE_SIZE']['attention_kib']:.0f} | {write_b:.4g} |", "",
-             "traffic_json: " + json.dumps(rec)]
+             f"| WRITE_SIZE | {out['WRITE_SIZE']['attention_kib']:.0f} | {write_b:.4g} |", ""]
+    # the step's copy kernels (their first dispatch, inside the step): scaled
+    # counter bytes against the bytes the method must move
+    from sequence_attention_video_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
+    one = wl.B * wl.T_pad * wl.H * wl.D * wl.eb               # one (B, T_pad, H, D) tensor
+    nrel = 2 if wl.cross else 3
+    tq = wl.q_tokens_pad if wl.cross else wl.T_pad
+    alg = {"send_kib": (f"send_recv_heads (`relayout_kernel`, {nrel} tensors)", nrel * one, nrel * one),
+           "gather_heads_kib": ("gather_heads (`gather_heads_kernel`)", one * tq // wl.T_pad, one * tq // wl.T_pad),
+           "gather_unpad_kib": ("gather_output_tokens (`gather_unpad_kernel`)",
+                                wl.B * (wl.Tq if wl.cross else wl.T) * wl.H * wl.D * wl.eb,
+                                wl.B * (wl.Tq if wl.cross else wl.T) * wl.H * wl.D * wl.eb)}
+    lines += ["Copy kernels of the step (first dispatch of each; scaled counter bytes against the algorithmic "
+              "bytes read and written):", "",
+              "| kernel | fetched (scaled) | algorithmic read | written (scaled) | algorithmic write |",
+              "|---|---|---|---|---|"]
+    for key, (label, rd, wr) in alg.items():
+        f_b = out["FETCH_SIZE"][key] * out["FETCH_SIZE"]["scale"] * 1024
+        w_b = out["WRITE_SIZE"][key] * out["WRITE_SIZE"]["scale"] * 1024
+        lines.append(f"| {label} | {f_b:.4g} | {rd:.4g} | {w_b:.4g} | {wr:.4g} |")
+    lines += ["", "traffic_json: " + json.dumps(rec)]
     path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
