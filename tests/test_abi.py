@@ -344,3 +344,22 @@ def test_tile_2d_relayout_heads_validation(lib):
     # nothing to move is a no-op
     assert call(src, dst, 3, 2, 4, 0, 16, 16, 24, H, D, b.SP_BF16, b.SP_HEADS_TO_TOKENS, T * H * D, hs,
                 None) == b.SP_OK
+
+
+def test_header_is_plain_c_and_links(tmp_path):
+    """include/sp.h compiles as C99 with every warning an error, and a C
+    program linked against libspattn.so runs the host-only entry points
+    (partition, optimal split, status strings, host-side argument checks)."""
+    gcc = shutil.which("gcc")
+    if gcc is None or not os.path.exists(LIB):
+        pytest.skip("gcc or the built library is missing")
+    exe = tmp_path / "c_consumer"
+    src = os.path.join(ROOT, "tests", "c_consumer.c")
+    libdir = os.path.dirname(LIB)
+    cmd = [gcc, "-std=c99", "-Wall", "-Wextra", "-Werror", "-pedantic", "-I", os.path.join(ROOT, "include"), src,
+           "-L", libdir, "-lspattn", "-Wl,-rpath," + libdir, "-o", str(exe)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True, timeout=60)
+    assert run.returncode == 0, run.stderr
+    assert "c consumer ok" in run.stdout
