@@ -75,7 +75,26 @@ def build(verbose: bool = True) -> str:
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")
+    build_native_consumer(verbose)
     return LIB
+
+
+NATIVE_SRC = os.path.join(ROOT, "tests", "native_step.cpp")
+NATIVE_BIN = os.path.join(ROOT, "tests", "bin", "native_step")
+
+
+def build_native_consumer(verbose: bool = True) -> str:
+    """Compile the test program that runs the whole path through the C ABI
+    alone (host code, linked against libspattn.so)."""
+    os.makedirs(os.path.dirname(NATIVE_BIN), exist_ok=True)
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-I", INCLUDE, NATIVE_SRC, "-L", PKG, "-lspattn",
+           f"-Wl,-rpath,{PKG}", "-o", NATIVE_BIN]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")
+    if verbose:
+        print(f"built {NATIVE_BIN}")
+    return NATIVE_BIN
 
 
 if __name__ == "__main__":
