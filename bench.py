@@ -922,6 +922,19 @@ def cpu_baseline(wl, x, budget_s: float, gpu_out=None):
     if gpu_out is not None:
         tol = 2e-2 if wl.dtype == "bf16" else 1e-4
         rec["timed_output_vs_oracle"] = {"rows": rows_done, "max_abs_err": err, "tol": tol, "ok": err <= tol}
+    # the copy oracle beside it: send_recv_heads of the relayed tensors (NumPy
+    # moves, one core), in the same bytes-moved terms as the GPU relayout
+    names = "kv" if wl.cross else "qkv"
+    c0 = time.perf_counter()
+    moved = 0
+    for n in names:
+        shards = O.token_shards(O.pad_tokens(x[n], Tp), W)
+        O.send_recv_heads(shards)
+        moved += 2 * shards.nbytes
+    dc = time.perf_counter() - c0
+    rec["relayout"] = {"value": round(moved / dc / 1e9, 3), "unit": "GB/s", "cores": 1, "kind": "oracle",
+                       "sample": f"send_recv_heads of {', '.join(names.upper())} (pad, token shards, exchange; "
+                                 f"{moved / 1e6:.1f} MB read + written), NumPy, {dc:.2f} s"}
     return rec
 
 
