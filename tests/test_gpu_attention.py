@@ -268,6 +268,15 @@ def test_attention_degenerate_inputs():
                            mask=torch.zeros(1, T, T, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert not raw(o).any()
+    # no keys at all (Tk = 0): every row is 0, in both kernels
+    o = sentinel_like((R, B, T, Hl, D), torch.bfloat16)
+    sp.sp_masked_attention(q, k, v, o, R, B, T, 0, Hl, D, st, st, st, st)
+    of = sentinel_like((R, B, T, Hl, D), torch.float32)
+    qf = q.float()
+    sp.sp_masked_attention(qf, qf.clone(), qf.clone(), of, R, B, T, 0, Hl, D, st, st, st, st)
+    torch.cuda.synchronize()
+    assert not raw(o).any()
+    assert not raw(of).any()
     # zero query rows / zero batches: nothing is written
     o = sentinel_like((R, B, T, Hl, D), torch.bfloat16)
     sp.sp_masked_attention(q, k, v, o, R, B, 0, T, Hl, D, st, st, st, st)
