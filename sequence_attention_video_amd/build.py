@@ -87,8 +87,8 @@ def build_native_consumer(verbose: bool = True) -> str:
     """Compile the test program that runs the whole path through the C ABI
     alone (host code, linked against libspattn.so)."""
     os.makedirs(os.path.dirname(NATIVE_BIN), exist_ok=True)
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-I", INCLUDE, NATIVE_SRC, "-L", PKG, "-lspattn",
-           f"-Wl,-rpath,{PKG}", "-o", NATIVE_BIN]
+    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O2", "-std=c++17", "-Xclang", "-target-feature", "-Xclang",
+           "-packed-fp32-ops", "-I", INCLUDE, NATIVE_SRC, "-L", PKG, "-lspattn", f"-Wl,-rpath,{PKG}", "-o", NATIVE_BIN]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError(f"compile failed: {' '.join(cmd)}\n{res.stdout}{res.stderr}")

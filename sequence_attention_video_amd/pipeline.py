@@ -265,6 +265,7 @@ class JointAVStep:
             x = inputs[name]
             q, k, v = (to_device(x[n], wl.dtype, device) for n in "qkv")
             self.steps[name] = UlyssesStep(wl, q, k, v, None, device=device)
+        self._streams = {name: torch.cuda.Stream(device=device) for name in self.PARTS}   # run_concurrent()
 
     def run(self) -> dict:
         return {name: self.steps[name].run() for name in self.PARTS}
@@ -280,8 +281,6 @@ class JointAVStep:
     CONCURRENT_ORDER = ("video_self", "a2v", "v2a", "audio_self")
 
     def run_concurrent(self) -> dict:
-        if not hasattr(self, "_streams"):
-            self._streams = {name: torch.cuda.Stream() for name in self.PARTS}
         cur = torch.cuda.current_stream()
         outs = {}
         for name in self.CONCURRENT_ORDER:
