@@ -53,6 +53,11 @@ MUTANTS = {
                                      "tile = grid[:, :1, i * th:(i + 1) * th, j * tw:(j + 1) * tw]"),
     "joint: cross keys from the wrong modality": ('(("v2a", audio_tokens, ta_pad, tv_pad),',
                                                  '(("v2a", video_tokens, tv_pad, tv_pad),'),
+    "row max over every key, hidden ones too": ("m = s.max(axis=1, keepdims=True)",
+                                                "m = ((q[i0:i1] @ k.T) * scale).max(axis=1, keepdims=True)"),
+    "key padding dropped under a user mask": ("vis = vis & (np.asarray(mask[i0:i1]) != 0)",
+                                              "vis = np.asarray(mask[i0:i1]) != 0"),
+    "batch 0's mask for every batch": ("mb = mask[bi if mask.shape[0] > 1 else 0][sel]", "mb = mask[0][sel]"),
 }
 
 
