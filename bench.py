@@ -231,6 +231,52 @@ def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
     print(open(path).read())
 
 
+PIPE_COUNTERS = ["SQ_VALU_MFMA_BUSY_CYCLES", "SQ_VALU_MFMA_COEXEC_CYCLES", "SQ_INSTS_VALU", "SQ_INSTS_MFMA",
+                 "SQ_INSTS_VALU_TRANS_F32", "SQ_INSTS_LDS", "SQ_WAIT_INST_LDS", "SQ_ACTIVE_INST_VALU",
+                 "GRBM_GUI_ACTIVE"]
+
+
+def write_pipe_summary(workload: str, pmc_dir: str, cmds: list):
+    """Turn one rocprofv3 --pmc pass (PIPE_COUNTERS) over `bench.py
+    --mfma-probe` into profiles/attention_pipes_<workload>.md: for the
+    all-ranks attention launch, the instructions issued per MFMA (VALU,
+    transcendental, LDS) and how much of the MFMA-busy time a VALU
+    instruction issued beside it (co-execution)."""
+    import collections
+    per = collections.defaultdict(dict)
+    kname = {}
+    for r in _counter_rows(pmc_dir):
+        d = int(r["Dispatch_Id"])
+        per[d][r["Counter_Name"]] = per[d].get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+        m = re.search(r"(attn_\w+<[^>]*>|\w+_kernel)\(", r["Kernel_Name"])
+        kname[d] = m.group(1) if m else r["Kernel_Name"][:60]
+    main = [d for d in sorted(per) if kname[d].startswith("attn_") and "combine" not in kname[d]]
+    n = (len(main) - 2) // 2
+    ds = main[1:1 + n]                      # the all-ranks launches after the step's own
+    avg = {c: sum(per[d].get(c, float("nan")) for d in ds) / len(ds) for c in PIPE_COUNTERS}
+    mf = avg["SQ_INSTS_MFMA"]
+    rows = [("VALU instructions per MFMA (SQ_INSTS_VALU / SQ_INSTS_MFMA)", avg["SQ_INSTS_VALU"] / mf),
+            ("transcendentals per MFMA (SQ_INSTS_VALU_TRANS_F32 / SQ_INSTS_MFMA)", avg["SQ_INSTS_VALU_TRANS_F32"] / mf),
+            ("LDS instructions per MFMA (SQ_INSTS_LDS / SQ_INSTS_MFMA)", avg["SQ_INSTS_LDS"] / mf),
+            ("MFMA-busy cycles with a VALU instruction issued beside them "
+             "(SQ_VALU_MFMA_COEXEC_CYCLES / SQ_VALU_MFMA_BUSY_CYCLES)",
+             avg["SQ_VALU_MFMA_COEXEC_CYCLES"] / avg["SQ_VALU_MFMA_BUSY_CYCLES"]),
+            ("MFMA busy of active cycles (SQ_VALU_MFMA_BUSY_CYCLES / 1024 SIMDs / (GRBM_GUI_ACTIVE / 8))",
+             avg["SQ_VALU_MFMA_BUSY_CYCLES"] / 1024 / (avg["GRBM_GUI_ACTIVE"] / 8))]
+    rec = {"workload": workload, "kernel": kname[ds[0]], "launches": len(ds),
+           "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
+           "counters_per_launch": {c: avg[c] for c in PIPE_COUNTERS}}
+    lines = [f"# Issue mix of the attention kernel on {workload}", "",
+             "Commands (run from the repository root on one MI355X):", "", "```"] + cmds + ["```", "",
+             f"All-ranks launch (`{rec['kernel']}`), averages over {len(ds)} launches (the probe's first, the step's, "
+             "left out). SQ instruction counts are wave instructions summed over the GPU.", "",
+             "| quantity | value |", "|---|---|"] + [f"| {q} | {v:.3f} |" for q, v in rows] +             ["", "pipe_json: " + json.dumps(rec)]
+    path = os.path.join(ROOT, "profiles", f"attention_pipes_{workload}.md")
+    with open(path, "w", encoding="utf-8") as f:
+        f.write("\n".join(lines) + "\n")
+    print(open(path).read())
+
+
 def _counter_rows(path):
     import csv
     import glob
@@ -351,6 +397,8 @@ def main():
                     help="run only the step and attention launches, all-ranks and one share (for the MFMA counter pass)")
     ap.add_argument("--write-mfma-summary", metavar="PMC_DIR",
                     help="write profiles/attention_mfma_<config>.md from one MFMA counter pass")
+    ap.add_argument("--write-pipe-summary", metavar="PMC_DIR",
+                    help="write profiles/attention_pipes_<config>.md from one issue-mix counter pass")
     ap.add_argument("--write-kernel-trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
                     help="write profiles/kernel_trace_<config>.md from a rocprofv3 --stats run of bench.py")
     ap.add_argument("--profile-command", action="append", default=[],
@@ -363,6 +411,9 @@ def main():
         write_kernel_trace_summary(*args.write_kernel_trace_summary,
                                    f"rocprofv3 kernel trace: bench step on {args.config}",
                                    "\n".join(args.profile_command), f"kernel_trace_{args.config}.md")
+        return
+    if args.write_pipe_summary:
+        write_pipe_summary(args.config, args.write_pipe_summary, args.profile_command)
         return
     if args.write_mfma_summary:
         write_mfma_summary(args.config, args.write_mfma_summary, args.profile_command)
