@@ -253,9 +253,10 @@ sp_status sp_tile_2d(const void* src, void* dst, int32_t split_h, int32_t split_
  * H % W != 0, n_tensors out of 1..3, negative sizes, split < 1, null,
  * misaligned (16 bytes) or overlapping pointers, head blocks that overlap,
  * grid_batch_stride < T*H*D -> SP_ERR_INVALID_ARG; Hl*D*element size not a
- * multiple of 16 bytes, more than 65535 rank x batch blocks, or an index space
- * (Tt*Hl*D or T*H*D 16-byte vectors per batch) of 2^32 or more ->
- * SP_ERR_UNSUPPORTED.
+ * multiple of 16 bytes, more than 65535 rank x batch blocks, T of 2^31 tokens
+ * or more, or more than 2^32 - 1024 16-byte vectors in one head-side segment
+ * (Tt*Hl*D elements) for SP_TOKENS_TO_HEADS or in one batch of the grid
+ * (T*H*D elements) for SP_HEADS_TO_TOKENS -> SP_ERR_UNSUPPORTED.
  */
 sp_status sp_tile_2d_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t split_h,
                                     int32_t split_w, int64_t B, int64_t F, int64_t height, int64_t width, int32_t H,
