@@ -93,15 +93,17 @@ sp_status sp_partition(int64_t total_tokens, int32_t world_size, int64_t* offset
  *   tail rows are written).  x and y may both be NULL (mask only); x may be
  *   NULL alone when T == 0 (y is then all zero bytes).
  * User mask (optional; mask_in and mask_out both NULL or both non-NULL):
- *   mask_in (B, T, T) uint8, 1 = may attend, packed; mask_out (B, T_pad, T_pad):
- *   the T x T block is copied, pad key columns are 0 for every row, and pad
- *   query rows see every real key and no pad key, so no row is left with
- *   nothing visible.  With no user mask the caller uses the key-only mask
- *   instead, i.e. kv_valid_len = T in sp_masked_attention.
+ *   mask_in (B, T, T) uint8, 1 = may attend, packed, 4-byte aligned;
+ *   mask_out (B, T_pad, T_pad), 16-byte aligned: the T x T block is copied,
+ *   pad key columns are 0 for every row, and pad query rows see every real
+ *   key and no pad key, so no row is left with nothing visible.  With no user
+ *   mask the caller uses the key-only mask instead, i.e. kv_valid_len = T in
+ *   sp_masked_attention.  The mask has the same B as the tokens: to extend
+ *   one mask shared by every batch, call with x = y = NULL and B = 1.
  * T_pad >= T is required (any value; divisibility is sp_partition's check).
- * Errors: SP_ERR_INVALID_ARG for negative sizes, T_pad < T, a bad stride or an
- * unpaired pointer; SP_ERR_UNSUPPORTED if C * element size is not a multiple
- * of 16 bytes.
+ * Errors: SP_ERR_INVALID_ARG for negative sizes, T_pad < T, a bad stride, an
+ * unpaired pointer, a misaligned or overlapping mask buffer;
+ * SP_ERR_UNSUPPORTED if C * element size is not a multiple of 16 bytes.
  */
 sp_status sp_pad(const void* x, int64_t x_batch_stride, void* y, int64_t B, int64_t T, int64_t T_pad,
                  int64_t C, sp_dtype dtype, const uint8_t* mask_in, uint8_t* mask_out, void* stream);
@@ -128,12 +130,59 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
                             sp_shard_strides tok, sp_shard_strides head, void* stream);
 
 /*
+ * sp_pad_relayout_heads -- pad_modality_for_uniform_sharding ([SP] 补齐)
+ * followed by send_recv_heads ([SP] 换头), as one move.
+ * src: n_tensors unpadded token tensors (B, T, H, D), batch b at base +
+ *   b*src_batch_stride (>= T*H*D), rows of H*D packed.
+ * dst: the head side of every rank, as in sp_relayout_heads: rank r, batch b
+ *   at base + r*head.rank + b*head.batch, (T_pad, Hl, D) packed.
+ * The bytes written are those of sp_pad (tail rows T..T_pad-1 zero) into a
+ * (B, T_pad, H, D) buffer, then sp_relayout_heads(SP_TOKENS_TO_HEADS) with
+ * rank s's token shard at rows s*Ts.. of that buffer (Ts = T_pad / W): head
+ * side row s*Ts + t of rank r holds head group r of token s*Ts + t, and zero
+ * bytes where s*Ts + t >= T.  The padded token tensor is never written.
+ * Errors: T_pad % W != 0 -> SP_ERR_NOT_DIVISIBLE; T_pad < T, H % W != 0,
+ * n_tensors out of 1..3, W < 1, negative sizes, null, misaligned (16 bytes)
+ * or overlapping pointers, head blocks that overlap, a bad batch stride ->
+ * SP_ERR_INVALID_ARG; Hl*D*element size not a multiple of 16 bytes, more than
+ * 65535 rank x batch blocks -> SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_pad_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                                int64_t B, int64_t T, int64_t T_pad, int32_t H, int32_t D, sp_dtype dtype,
+                                int64_t src_batch_stride, sp_shard_strides head, void* stream);
+
+/*
+ * sp_gather_heads_unpad -- gather_heads ([SP] 换头, the swap back) followed by
+ * gather_output_tokens ([SP] 还原), as one move.
+ * src: the head side of every rank (B, T_pad, Hl, D) at base + r*head.rank +
+ *   b*head.batch (as sp_relayout_heads writes it).
+ * dst: out (B, T, H, D), packed.
+ * The bytes written are those of sp_relayout_heads(SP_HEADS_TO_TOKENS) into a
+ * stacked token side (W, B, Ts, H, D), then sp_gather_unpad with the same
+ * counts: rank s keeps its first counts[s] token rows (counts: host array of
+ * W entries, or NULL for Ts each), the kept rows are concatenated in rank
+ * order and the first T form out.  The token side is never written.
+ * Errors: T_pad % W != 0 -> SP_ERR_NOT_DIVISIBLE; H % W != 0, counts[s]
+ * outside 0..Ts, sum(counts) < T, n_tensors out of 1..3, negative sizes, null,
+ * misaligned (16 bytes) or overlapping pointers, head blocks that overlap ->
+ * SP_ERR_INVALID_ARG; W > 128, Hl*D*element size not a multiple of 16 bytes,
+ * B > 65535 -> SP_ERR_UNSUPPORTED.
+ */
+sp_status sp_gather_heads_unpad(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                                int64_t B, int64_t T_pad, int32_t H, int32_t D, sp_dtype dtype,
+                                sp_shard_strides head, const int64_t* counts, int64_t T, void* stream);
+
+/*
  * sp_masked_attention -- attention on the local heads ([SP] 换头, computed in
  * place on each rank; masks as defined in [SP] 补齐).
  * For R rank shares, B batches, Hl heads: query i attends key j iff
  *   j < kv_valid_len, and, if mask != NULL, mask[b, i, j] != 0.
  * o = softmax(scale * q k^T) v over the visible keys, accumulated in float32;
- * a query row with no visible key gets 0 (never NaN).
+ * a query row with no visible key gets 0 (never NaN).  scale must be a
+ * positive, finite, normal float whose product with log2(e) is normal too
+ * (the path passes 1/sqrt(D)): the kernels hide a key by giving its raw
+ * score -inf and take the row maximum of raw scores, which both need a
+ * positive factor.  Scores are assumed finite.
  * q: (R, B, Tq, Hl, D) with strides qs; k, v: (R, B, Tk, Hl, D) with ks, vs;
  * o: (R, B, Tq, Hl, D) with os (o must not overlap q, k or v).  d is
  * contiguous for all four.  Base pointers and strides must keep every 16-byte
@@ -152,11 +201,13 @@ sp_status sp_relayout_heads(const void* const* src, void* const* dst, int32_t n_
  * partial results.  Without room for them (NULL or a smaller workspace) the
  * same call runs unsplit: same result up to float32 summation order, slower
  * on such shapes.
- * Supported: SP_BF16 with D in {64, 128} (bf16 MFMA, float32 softmax and
- * accumulation, output rounded to nearest even) and SP_F32 with D in
- * {16, 64, 128} (float32 MFMA throughout).
- * Errors: sizes < 0, null tensors, kv_valid_len < 0, a mask without a large
- * enough workspace -> SP_ERR_INVALID_ARG; other D, or (bf16) a K or V token
+ * Supported: D in {16, 64, 128} for both types.  SP_BF16 at D = 64 and 128
+ * runs bf16 MFMA with float32 softmax and accumulation; SP_BF16 at D = 16
+ * widens the bf16 values exactly to float32 and runs float32 MFMA; SP_F32
+ * runs float32 MFMA throughout.  bf16 outputs are rounded to nearest even.
+ * Errors: sizes < 0, null tensors, kv_valid_len < 0, scale outside the range
+ * above, a mask without a large enough workspace -> SP_ERR_INVALID_ARG;
+ * other D, or (bf16, D = 64 or 128) a K or V token
  * stride above 8 million elements (its 32-bit tile offsets), or (bf16) a user
  * mask with Tk above 4096 * 64 keys (the per-row tile classes it keeps in
  * LDS), or a user mask with B above 65535 or Tq above 65535 query tiles

@@ -26,7 +26,7 @@ SP_GRID_TO_TILES, SP_TILES_TO_GRID = 0, 1
 EXPORTS = (
     "sp_status_string", "sp_version", "sp_partition", "sp_pad", "sp_relayout_heads",
     "sp_masked_attention_workspace_size", "sp_masked_attention", "sp_gather_unpad", "sp_optimal_split",
-    "sp_tile_2d", "sp_tile_2d_relayout_heads",
+    "sp_tile_2d", "sp_tile_2d_relayout_heads", "sp_pad_relayout_heads", "sp_gather_heads_unpad",
 )
 
 
@@ -80,6 +80,12 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sp_tile_2d_relayout_heads.restype = ctypes.c_int
     lib.sp_tile_2d_relayout_heads.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i32, i64, i64, i64,
                                               i64, i32, i32, ctypes.c_int, ctypes.c_int, i64, ShardStrides, vp]
+    lib.sp_pad_relayout_heads.restype = ctypes.c_int
+    lib.sp_pad_relayout_heads.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i64, i64, i64, i32, i32,
+                                          ctypes.c_int, i64, ShardStrides, vp]
+    lib.sp_gather_heads_unpad.restype = ctypes.c_int
+    lib.sp_gather_heads_unpad.argtypes = [ctypes.POINTER(vp), ctypes.POINTER(vp), i32, i32, i64, i64, i32, i32,
+                                          ctypes.c_int, ShardStrides, ctypes.POINTER(i64), i64, vp]
     if path is None:
         _lib = lib
     return lib
@@ -157,6 +163,16 @@ def sp_pad(x, y, T_pad: int, mask_in=None, mask_out=None, x_batch_stride: int | 
     else:
         B, C, dt, xbs = mask_in.shape[0], 0, SP_F32, 0
         T = mask_in.shape[1] if T is None else T
+    if (mask_in is None) != (mask_out is None):
+        raise ValueError("mask_in and mask_out go together")
+    if mask_in is not None:
+        # the library reads B*T*T mask bytes and writes B*T_pad*T_pad: both
+        # buffers must hold exactly that (one shared mask: extend it alone)
+        if tuple(mask_in.shape) != (B, T, T) or not mask_in.is_contiguous():
+            raise ValueError(f"mask_in must be a packed ({B}, {T}, {T}) tensor, got {tuple(mask_in.shape)}")
+        if tuple(mask_out.shape) != (B, T_pad, T_pad) or not mask_out.is_contiguous():
+            raise ValueError(f"mask_out must be a packed ({B}, {T_pad}, {T_pad}) tensor, "
+                             f"got {tuple(mask_out.shape)}")
     check(load().sp_pad(_ptr(x), int(xbs), _ptr(y), int(B), int(T), int(T_pad), int(C), dt,
                         _ptr(mask_in), _ptr(mask_out), _stream(stream)))
 
@@ -268,3 +284,42 @@ def sp_tile_2d_relayout_heads(src, dst, split_h: int, split_w: int, B: int, F: i
     check(load().sp_tile_2d_relayout_heads(sp, dp, n, int(split_h), int(split_w), int(B), int(F), int(height),
                                            int(width), int(H), int(D), _dtype_code(src[0]), int(direction), int(gbs),
                                            ShardStrides(*head), _stream(stream)))
+
+
+def _ptr_array(ts):
+    return (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+
+
+def sp_pad_relayout_heads(src, dst, W: int, B: int, T: int, T_pad: int, H: int, D: int,
+                          src_batch_stride=None, head_strides=None, stream=None):
+    """pad_modality_for_uniform_sharding + send_recv_heads as one move.
+    ``src``: 1..3 unpadded token tensors (B, T, H, D); ``dst``: as many head
+    sides, stacked (W, B, T_pad, Hl, D) unless ``head_strides`` is given."""
+    src, dst = list(src), list(dst)
+    _cuda(*src, *dst)
+    if len(dst) != len(src):
+        raise ValueError("one destination per source")
+    Hl = H // max(W, 1)
+    sbs = src_batch_stride if src_batch_stride is not None else src[0].stride(0)
+    head = head_strides or (B * T_pad * Hl * D, T_pad * Hl * D)
+    check(load().sp_pad_relayout_heads(_ptr_array(src), _ptr_array(dst), len(src), int(W), int(B), int(T),
+                                       int(T_pad), int(H), int(D), _dtype_code(src[0]), int(sbs),
+                                       ShardStrides(*head), _stream(stream)))
+
+
+def sp_gather_heads_unpad(src, dst, W: int, B: int, T_pad: int, H: int, D: int, T: int, counts=None,
+                          head_strides=None, stream=None):
+    """gather_heads + gather_output_tokens as one move: 1..3 head sides
+    (W, B, T_pad, Hl, D) -> as many outputs (B, T, H, D)."""
+    src, dst = list(src), list(dst)
+    _cuda(*src, *dst)
+    if len(dst) != len(src):
+        raise ValueError("one destination per source")
+    Hl = H // max(W, 1)
+    head = head_strides or (B * T_pad * Hl * D, T_pad * Hl * D)
+    carr = None
+    if counts is not None:
+        carr = (ctypes.c_int64 * len(counts))(*[int(c) for c in counts])
+    check(load().sp_gather_heads_unpad(_ptr_array(src), _ptr_array(dst), len(src), int(W), int(B), int(T_pad),
+                                       int(H), int(D), _dtype_code(src[0]), ShardStrides(*head), carr, int(T),
+                                       _stream(stream)))

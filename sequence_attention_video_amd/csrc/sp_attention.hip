@@ -736,9 +736,33 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
 
 // ---------------------------------------------------------------- fp32 kernel
 
+// Element access of the fp32-MFMA kernel: float storage, or bfloat16 storage
+// (E = uint16_t bit patterns) widened exactly to float on load and rounded to
+// nearest even on store.  The bf16 form serves the head dims the bf16 MFMA
+// kernel is not built for (D = 16).
+__device__ __forceinline__ float widen(float x) { return x; }
+__device__ __forceinline__ float widen(uint16_t x) { return __uint_as_float(uint32_t(x) << 16); }
+__device__ __forceinline__ void narrow_store(float* p, float x) { *p = x; }
+__device__ __forceinline__ void narrow_store(uint16_t* p, float x) {
+  *reinterpret_cast<__bf16*>(p) = static_cast<__bf16>(x);
+}
+// four consecutive elements (16-byte aligned for float, 8-byte for bf16)
+__device__ __forceinline__ void load4(const float* p, float (&o)[4]) {
+  const u32x4 v = *reinterpret_cast<const u32x4*>(p);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = __uint_as_float(v[i]);
+}
+__device__ __forceinline__ void load4(const uint16_t* p, float (&o)[4]) {
+  const uint2 v = *reinterpret_cast<const uint2*>(p);
+  o[0] = __uint_as_float(v.x << 16);
+  o[1] = __uint_as_float(v.x & 0xffff0000u);
+  o[2] = __uint_as_float(v.y << 16);
+  o[3] = __uint_as_float(v.y & 0xffff0000u);
+}
+
 // Same structure with v_mfma_f32_32x32x2f32: each k-step contracts two values,
 // one per lane half.  V needs no transpose (one element per lane per step).
-template <int D, bool MASK>
+template <int D, bool MASK, typename E>
 __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   static_assert(D % 16 == 0, "f32 path needs D divisible by 16");
   constexpr int KST = D + 1;                 // odd stride: column reads hit distinct banks
@@ -751,16 +775,16 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, h = lane >> 5;
 
-  const float* qp = static_cast<const float*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
-  const float* kp = static_cast<const float*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
-  const float* vp = static_cast<const float*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
-  float* op = static_cast<float*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
+  const E* qp = static_cast<const E*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
+  const E* kp = static_cast<const E*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
+  const E* vp = static_cast<const E*>(a.v) + tc.r * a.vs[0] + tc.b * a.vs[1] + tc.head * a.vs[3];
+  E* op = static_cast<E*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3];
 
   const int64_t qrow = int64_t(tc.qt) * BM32 + w * 32 + l32;
   const bool qvalid = qrow < a.Tq;
   float qf[D / 2];
 #pragma unroll
-  for (int s = 0; s < D / 2; ++s) qf[s] = qvalid ? qp[qrow * a.qs[2] + 2 * s + h] : 0.f;
+  for (int s = 0; s < D / 2; ++s) qf[s] = qvalid ? widen(qp[qrow * a.qs[2] + 2 * s + h]) : 0.f;
 
   f32x16 oacc[NDB];
 #pragma unroll
@@ -787,15 +811,15 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
     __syncthreads();
     for (int c = tid; c < BN * D / 4; c += kThreads) {
       const int n = c / (D / 4), dc = c % (D / 4);
-      u32x4 kv = u32x4{0, 0, 0, 0}, vv = u32x4{0, 0, 0, 0};
+      float kv[4] = {0.f, 0.f, 0.f, 0.f}, vv[4] = {0.f, 0.f, 0.f, 0.f};
       if (key0 + n < a.Tk) {
-        kv = *reinterpret_cast<const u32x4*>(kp + (key0 + n) * a.ks[2] + 4 * dc);
-        vv = *reinterpret_cast<const u32x4*>(vp + (key0 + n) * a.vs[2] + 4 * dc);
+        load4(kp + (key0 + n) * a.ks[2] + 4 * dc, kv);
+        load4(vp + (key0 + n) * a.vs[2] + 4 * dc, vv);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        k_lds[n * KST + 4 * dc + i] = __uint_as_float(kv[i]);
-        v_lds[n * VST + 4 * dc + i] = __uint_as_float(vv[i]);
+        k_lds[n * KST + 4 * dc + i] = kv[i];
+        v_lds[n * VST + 4 * dc + i] = vv[i];
       }
     }
     __syncthreads();
@@ -863,7 +887,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   const float lt = l_run + __shfl_xor(l_run, 32);
   const float inv = lt > 0.f ? 1.0f / lt : 0.f;
   if (qvalid) {
-    float* orow = op + qrow * a.os[2];
+    E* orow = op + qrow * a.os[2];
 #pragma unroll
     for (int d = 0; d < NDB; ++d) {
 #pragma unroll
@@ -871,7 +895,7 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
         const int dim = 32 * d + 8 * g + 4 * h;
         if (dim < D) {
 #pragma unroll
-          for (int i = 0; i < 4; ++i) orow[dim + i] = oacc[d][4 * g + i] * inv;
+          for (int i = 0; i < 4; ++i) narrow_store(orow + dim + i, oacc[d][4 * g + i] * inv);
         }
       }
     }
@@ -981,9 +1005,13 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
   return x < y + nb && y < x + na;
 }
 
+// The bf16 MFMA kernel is built for D = 64 and 128; bf16 at D = 16 runs the
+// fp32-MFMA kernel on widened values (exact products, float32 accumulation).
+bool bf16_mfma_kernel(sp_dtype dt, int32_t D) { return dt == SP_BF16 && (D == 64 || D == 128); }
+
 template <int D, bool MASK>
 void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
-  if (dt == SP_BF16) {
+  if (bf16_mfma_kernel(dt, D)) {
     if constexpr (D % 32 == 0) {
       if (a.part) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
@@ -993,18 +1021,17 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(64 * kWaves<D>), 0, s, a);
       }
     }
+  } else if (dt == SP_BF16) {
+    hipLaunchKernelGGL((attn_f32_kernel<D, MASK, uint16_t>), dim3(a.nwg), dim3(kThreads), 0, s, a);
   } else {
-    hipLaunchKernelGGL((attn_f32_kernel<D, MASK>), dim3(a.nwg), dim3(kThreads), 0, s, a);
+    hipLaunchKernelGGL((attn_f32_kernel<D, MASK, float>), dim3(a.nwg), dim3(kThreads), 0, s, a);
   }
 }
 
 template <bool MASK>
 sp_status dispatch_d(int D, const AttnArgs& a, sp_dtype dt, hipStream_t s) {
   switch (D) {
-    case 16:
-      if (dt == SP_BF16) return SP_ERR_UNSUPPORTED;
-      launch_attn<16, MASK>(a, dt, s);
-      break;
+    case 16: launch_attn<16, MASK>(a, dt, s); break;
     case 64: launch_attn<64, MASK>(a, dt, s); break;
     case 128: launch_attn<128, MASK>(a, dt, s); break;
     default: return SP_ERR_UNSUPPORTED;
@@ -1053,9 +1080,12 @@ int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D, b
 // query rows per workgroup of the bf16 kernel for head dim D (64 or 128)
 int64_t bf16_rows(int32_t D) { return D == 64 ? kRows<64> : kRows<128>; }
 
+// query rows per workgroup of the kernel a launch runs
+int64_t kernel_rows(sp_dtype dtype, int32_t D) { return bf16_mfma_kernel(dtype, D) ? bf16_rows(D) : BM32; }
+
 // height of the mask-class tiles of a launch: the bf16 kernel's query tile,
-// or kClsRowsF32 for the fp32 kernel
-int64_t cls_rows(sp_dtype dtype, int32_t D) { return dtype == SP_BF16 ? bf16_rows(D) : kClsRowsF32; }
+// or kClsRowsF32 for the fp32-MFMA kernel
+int64_t cls_rows(sp_dtype dtype, int32_t D) { return bf16_mfma_kernel(dtype, D) ? bf16_rows(D) : kClsRowsF32; }
 
 // bytes of partial records of a split launch: two slots per workgroup
 int64_t split_bytes(int64_t ncu, int32_t D) { return 2 * ncu * bf16_rows(D) * (int64_t(D) + 2) * 4; }
@@ -1084,7 +1114,7 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   // range needs no more)
   const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask != 0, mask_batch_stride, cls_rows(dtype, D));
   int64_t split = 0;
-  if (dtype == SP_BF16 && (D == 64 || D == 128)) {
+  if (bf16_mfma_kernel(dtype, D)) {
     const int64_t ncu = device_cus();
     const int64_t items = div_up(Tq, bf16_rows(D)) * Hl * B * R;
     if (split_units_per_wg(items, div_up(Tk, KT), ncu, D, has_mask != 0)) split = split_bytes(ncu, D);
@@ -1092,18 +1122,39 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
   return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
 }
 
-extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
-                                         const void* v, sp_attn_strides vs, void* o, sp_attn_strides os,
-                                         int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
-                                         sp_dtype dtype, int64_t kv_valid_len, const uint8_t* mask,
-                                         int64_t mask_batch_stride, float scale, void* workspace,
-                                         size_t workspace_bytes, void* stream) {
+namespace {
+
+// One attention call after the host-side checks: the launch arguments and
+// what the launch needs from the workspace.  Built without any HIP call.
+struct AttnCall {
+  AttnArgs a;
+  sp_dtype dtype;
+  int32_t D;
+  bool empty;          // nothing to compute (a size is 0)
+  bool has_mask;
+  int64_t mask_bytes;  // class bytes and visibility words (0 without a mask)
+  int64_t crows;       // class-tile height
+  int64_t nqt_cls, nkt, nwg;
+  int64_t bm;          // masks in the workspace: B per-batch masks, or 1 shared
+};
+
+// Every check of sp_masked_attention that does not concern the workspace.
+sp_status attn_check(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks, const void* v,
+                     sp_attn_strides vs, void* o, sp_attn_strides os, int32_t R, int64_t B, int64_t Tq, int64_t Tk,
+                     int32_t Hl, int32_t D, sp_dtype dtype, int64_t kv_valid_len, const uint8_t* mask,
+                     int64_t mask_batch_stride, float scale, AttnCall& c) {
   if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
   if (R < 0 || B < 0 || Tq < 0 || Tk < 0 || Hl < 0 || kv_valid_len < 0 || mask_batch_stride < 0)
     return SP_ERR_INVALID_ARG;
-  if (!(D == 16 || D == 64 || D == 128) || (dtype == SP_BF16 && D == 16)) return SP_ERR_UNSUPPORTED;
-  if (!std::isfinite(scale)) return SP_ERR_INVALID_ARG;
-  if (R == 0 || B == 0 || Tq == 0 || Hl == 0) return SP_OK;
+  if (!(D == 16 || D == 64 || D == 128)) return SP_ERR_UNSUPPORTED;
+  // The kernels hide a key by setting its raw score q.k to -inf and take the
+  // row maximum of raw scores before multiplying by scale * log2(e): both are
+  // right only for a positive factor, and a zero or denormal factor would turn
+  // -inf * 0 into NaN.  The softmax scale of the path is 1/sqrt(D).
+  const float c2 = scale * 1.4426950408889634f;
+  if (!std::isfinite(scale) || !(scale > 0.f) || !std::isnormal(c2) || !std::isnormal(scale)) return SP_ERR_INVALID_ARG;
+  c.empty = R == 0 || B == 0 || Tq == 0 || Hl == 0;
+  if (c.empty) return SP_OK;
   if (!q || !k || !v || !o) return SP_ERR_INVALID_ARG;
   if (!nonneg(qs) || !nonneg(ks) || !nonneg(vs) || !nonneg(os)) return SP_ERR_INVALID_ARG;
   const int64_t eb = elem_bytes(dtype);
@@ -1116,24 +1167,22 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   if (overlap(o, on, q, span_bytes(qs, R, B, Tq, Hl, D, eb)) || overlap(o, on, k, span_bytes(ks, R, B, tk1, Hl, D, eb)) ||
       overlap(o, on, v, span_bytes(vs, R, B, tk1, Hl, D, eb)))
     return SP_ERR_INVALID_ARG;
+  const bool mfma16 = bf16_mfma_kernel(dtype, D);
   const int64_t crows = cls_rows(dtype, D);
-  const int64_t nqt = div_up(Tq, dtype == SP_BF16 ? bf16_rows(D) : BM32), nkt = div_up(Tk, BN);
+  const int64_t nqt = div_up(Tq, kernel_rows(dtype, D)), nkt = div_up(Tk, BN);
   const int64_t nqt_cls = div_up(Tq, crows);
   const int64_t nwg = nqt * Hl * B * R;
   if (nwg >= (int64_t(1) << 31) || nkt >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
   // the bf16 kernel addresses one key tile of K and of V with 32-bit byte offsets
-  if (dtype == SP_BF16 && ((KT - 1) * (ks.token > vs.token ? ks.token : vs.token) + D) * eb >= (int64_t(1) << 31))
+  if (mfma16 && ((KT - 1) * (ks.token > vs.token ? ks.token : vs.token) + D) * eb >= (int64_t(1) << 31))
     return SP_ERR_UNSUPPORTED;
   const bool has_mask = mask != nullptr && Tk > 0;
-  if (dtype == SP_BF16 && has_mask && nkt > kMaxClassTiles) return SP_ERR_UNSUPPORTED;
-  const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride, crows);
-  if (has_mask && (workspace == nullptr || workspace_bytes < size_t(mask_bytes))) return SP_ERR_INVALID_ARG;
-  if (has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
+  if (mfma16 && has_mask && nkt > kMaxClassTiles) return SP_ERR_UNSUPPORTED;
   // (grid limits; nqt_cls also keeps the visibility-word offsets, below
   // 2 * 8 * ldw bytes, inside 32 bits)
   if (has_mask && (B > 65535 || nqt_cls > 65535)) return SP_ERR_UNSUPPORTED;
 
-  AttnArgs a;
+  AttnArgs& a = c.a;
   a.q = q; a.k = k; a.v = v; a.o = o;
   const sp_attn_strides* src[4] = {&qs, &ks, &vs, &os};
   int64_t* dst[4] = {a.qs, a.ks, a.vs, a.os};
@@ -1143,39 +1192,71 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
   a.B = B; a.Tq = Tq; a.Tk = Tk; a.Hl = Hl;
   a.kv_end = kv_valid_len < Tk ? kv_valid_len : Tk;
   a.mask = mask; a.mask_bs = mask_batch_stride;
-  a.cls = static_cast<const uint8_t*>(workspace);
-  {
-    const int64_t bm = mask_batch_stride ? B : 1;
-    a.bits = reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) + cls_ws_bytes(bm, Tq, Tk, crows));
-  }
+  a.cls = nullptr; a.bits = nullptr;
   a.ldw = div_up(Tq, 2) * 2;
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
-  a.c = scale * 1.4426950408889634f;
+  a.c = c2;
   a.nwg = uint32_t(nwg);
   a.units = 0; a.upw = 0; a.nku = 0; a.part = nullptr;
-  if (dtype == SP_BF16) {
+  c.dtype = dtype;
+  c.D = D;
+  c.has_mask = has_mask;
+  c.crows = crows;
+  c.nqt_cls = nqt_cls;
+  c.nkt = nkt;
+  c.nwg = nwg;
+  c.bm = mask_batch_stride ? B : 1;
+  c.mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask, mask_batch_stride, crows);
+  return SP_OK;
+}
+
+// Checks the workspace, decides the split and launches: the mask classifier
+// (with a user mask), then the attention kernel (and the merge of a split
+// launch).
+sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStream_t s) {
+  AttnArgs& a = c.a;
+  if (c.has_mask && (workspace == nullptr || workspace_bytes < size_t(c.mask_bytes))) return SP_ERR_INVALID_ARG;
+  if (c.has_mask && (reinterpret_cast<uintptr_t>(workspace) & 255) != 0) return SP_ERR_INVALID_ARG;
+  a.cls = static_cast<const uint8_t*>(workspace);
+  a.bits = c.has_mask ? reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) +
+                                                          cls_ws_bytes(c.bm, a.Tq, a.Tk, c.crows))
+                      : nullptr;
+  if (bf16_mfma_kernel(c.dtype, c.D)) {
     const int64_t ncu = device_cus();
     const int64_t nku = div_up(a.kv_end, KT);
-    const int64_t upw = split_units_per_wg(nwg, nku, ncu, D, has_mask);
+    const int64_t upw = split_units_per_wg(c.nwg, nku, ncu, c.D, c.has_mask);
     // the split runs only with room for its partial records after the mask
     // part (as sized by sp_masked_attention_workspace_size); otherwise the
     // plain launch runs
-    const int64_t part_at = (mask_bytes + 255) / 256 * 256;
-    if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, D)) &&
+    const int64_t part_at = (c.mask_bytes + 255) / 256 * 256;
+    if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, c.D)) &&
         (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
-      a.units = nwg * nku; a.upw = upw; a.nku = int32_t(nku);
+      a.units = c.nwg * nku; a.upw = upw; a.nku = int32_t(nku);
       a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_at);
     }
   }
-  hipStream_t s = as_stream(stream);
-  if (has_mask) {
-    const int64_t bm = mask_batch_stride ? B : 1;
-    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(div_up(nkt, kClsSpan)), unsigned(nqt_cls), unsigned(bm)),
+  if (c.has_mask) {
+    hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(div_up(c.nkt, kClsSpan)), unsigned(c.nqt_cls), unsigned(c.bm)),
                        dim3(kClsThreads), 0,
-                       s, mask, mask_batch_stride, Tq, Tk, int32_t(nqt_cls), int32_t(nkt),
-                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw, int32_t(crows));
+                       s, a.mask, a.mask_bs, a.Tq, a.Tk, int32_t(c.nqt_cls), int32_t(c.nkt),
+                       static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw, int32_t(c.crows));
     if (launch_status() != SP_OK) return SP_ERR_HIP;
-    return dispatch_d<true>(D, a, dtype, s);
+    return dispatch_d<true>(c.D, a, c.dtype, s);
   }
-  return dispatch_d<false>(D, a, dtype, s);
+  return dispatch_d<false>(c.D, a, c.dtype, s);
+}
+
+}  // namespace
+
+extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
+                                         const void* v, sp_attn_strides vs, void* o, sp_attn_strides os,
+                                         int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
+                                         sp_dtype dtype, int64_t kv_valid_len, const uint8_t* mask,
+                                         int64_t mask_batch_stride, float scale, void* workspace,
+                                         size_t workspace_bytes, void* stream) {
+  AttnCall c;
+  const sp_status st = attn_check(q, qs, k, ks, v, vs, o, os, R, B, Tq, Tk, Hl, D, dtype, kv_valid_len, mask,
+                                  mask_batch_stride, scale, c);
+  if (st != SP_OK || c.empty) return st;
+  return attn_run(c, workspace, workspace_bytes, as_stream(stream));
 }

@@ -44,13 +44,17 @@ struct RelayoutArgs {
   uint32_t n_per_seg;                            // Ts*V vectors per (tensor, r, b, s)
   uint32_t chunks;                               // workgroups per segment
   int to_heads;                                  // 1: token side -> head side
+  int64_t Ts;                                    // tokens per rank shard
+  int64_t valid;                                 // to heads: token rows s*Ts + t >= valid are zero
 };
 
 // blockIdx.x = (source-token rank s, chunk), blockIdx.y = (head-group rank r,
 // batch b), blockIdx.z = tensor.  On the head side the segment (r, b, s) is
 // one contiguous block of Ts runs; on the token side each run sits inside a
 // token row at offset r*run_b.  Flat vector f of the segment is token t = f/V,
-// vector f%V of the run.
+// vector f%V of the run.  Toward the head side, token rows at or past `valid`
+// (the pad rows of 补齐) are written as zero bytes and never read, so an
+// unpadded token tensor is padded and exchanged in the same move.
 __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
   const uint32_t s = blockIdx.x / a.chunks;
   const uint32_t chunk = blockIdx.x - s * a.chunks;
@@ -75,7 +79,8 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
       const int64_t head = head_off + int64_t(f) * 16;
       const int64_t raddr = a.to_heads ? tok : head;
       waddr[u] = a.to_heads ? head : tok;
-      buf[u] = load16(src + raddr);
+      buf[u] = vec16{0, 0, 0, 0};
+      if (!a.to_heads || int64_t(s) * a.Ts + t < a.valid) buf[u] = load16(src + raddr);
     }
   }
 #pragma unroll
@@ -132,6 +137,55 @@ __global__ __launch_bounds__(kThreads) void gather_heads_kernel(GatherHeadsArgs 
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t f = f0 + u * kThreads;
     if (f < a.n_per_shard) store16(dst + int64_t(f) * 16, buf[u]);
+  }
+}
+
+// gather_heads followed by gather_output_tokens as one move: rank s's token
+// rows after the swap back, trimmed to its first counts[s] rows, land at row
+// cum[s] of the output (B, T, H, D), and rows from T on are dropped.  Walked
+// from the output side like gather_heads_kernel (whole output rows per
+// workgroup, 1 KiB wave stores each fed by one run of one head-side rank).
+constexpr int kMaxWorldFused = 128;
+struct GatherHeadsUnpadArgs {
+  const char* src[3];
+  char* dst[3];
+  int64_t head_rank_b, head_batch_b;  // head side (bytes)
+  int64_t run_b;                      // Hl*D*eb
+  int64_t seg_b;                      // Ts*run_b
+  int64_t out_batch_b, row_b;         // output: T*H*D*eb per batch, H*D*eb per row
+  uint32_t V;
+  FastDiv fdV, fdRow;                 // by V and by W*V
+  uint32_t chunks;                    // workgroups per rank (for the longest kept piece)
+  int64_t cum[kMaxWorldFused + 1];    // output row of each rank's first kept row
+  uint32_t n_vec[kMaxWorldFused];     // kept rows * W*V of each rank (after the unpad)
+};
+
+__global__ __launch_bounds__(kThreads) void gather_heads_unpad_kernel(GatherHeadsUnpadArgs a) {
+  const uint32_t s = blockIdx.x / a.chunks;
+  const uint32_t chunk = blockIdx.x - s * a.chunks;
+  const int64_t b = blockIdx.y;
+  const int n = blockIdx.z;
+  const uint32_t nv = a.n_vec[s];
+  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
+  if (chunk * uint32_t(kChunk) >= nv) return;
+  const char* src = a.src[n] + b * a.head_batch_b + int64_t(s) * a.seg_b;
+  char* dst = a.dst[n] + b * a.out_batch_b + a.cum[s] * a.row_b;
+  vec16 buf[kUnroll];
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < nv) {
+      const uint32_t t = fdiv(f, a.fdRow);
+      const uint32_t rem = f - t * a.fdRow.d;
+      const uint32_t r = fdiv(rem, a.fdV);
+      const uint32_t v = rem - r * a.V;
+      buf[u] = load16(src + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16);
+    }
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const uint32_t f = f0 + u * kThreads;
+    if (f < nv) store16(dst + int64_t(f) * 16, buf[u]);
   }
 }
 
@@ -470,7 +524,9 @@ extern "C" sp_status sp_pad(const void* x, int64_t x_batch_stride, void* y, int6
     const uint8_t* ie = mask_in + B * T * T;
     const uint8_t* oe = mask_out + B * T_pad * T_pad;
     if (B > 0 && T > 0 && mask_in < oe && mask_out < ie) return SP_ERR_INVALID_ARG;
-    if (!aligned16(mask_out)) return SP_ERR_INVALID_ARG;
+    // the mask kernel reads the input as 4-byte words (a word holding the
+    // mask's first byte starts at mask_in itself)
+    if (!aligned16(mask_out) || (reinterpret_cast<uintptr_t>(mask_in) & 3u) != 0) return SP_ERR_INVALID_ARG;
   }
   hipStream_t s = as_stream(stream);
   if (tokens && B > 0 && T_pad * C > 0) {
@@ -585,10 +641,140 @@ extern "C" sp_status sp_relayout_heads(const void* const* src, void* const* dst,
   a.n_per_seg = uint32_t(Ts * V);
   a.chunks = uint32_t(div_up(Ts * V, kChunk));
   a.to_heads = dir == SP_TOKENS_TO_HEADS;
+  a.Ts = Ts;
+  a.valid = T_pad;
   const int64_t gx = int64_t(a.chunks) * W;
   if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
   dim3 grid(unsigned(gx), unsigned(W * B), unsigned(n_tensors));
   hipLaunchKernelGGL(relayout_kernel, grid, dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+// Host checks shared by the two fused moves: the tensor lists, and that no
+// destination overlaps a source or another destination (spans in bytes).
+static sp_status check_tensor_lists(const void* const* src, void* const* dst, int32_t n_tensors, int64_t s_span,
+                                    int64_t d_span) {
+  if (n_tensors < 1 || n_tensors > 3 || src == nullptr || dst == nullptr) return SP_ERR_INVALID_ARG;
+  for (int i = 0; i < n_tensors; ++i) {
+    if (src[i] == nullptr || dst[i] == nullptr || !aligned16(src[i]) || !aligned16(dst[i])) return SP_ERR_INVALID_ARG;
+  }
+  for (int i = 0; i < n_tensors && s_span > 0 && d_span > 0; ++i) {
+    const char* d0 = static_cast<const char*>(dst[i]);
+    for (int j = 0; j < n_tensors; ++j) {
+      const char* s0 = static_cast<const char*>(src[j]);
+      if (s0 < d0 + d_span && d0 < s0 + s_span) return SP_ERR_INVALID_ARG;
+      const char* d1 = static_cast<const char*>(dst[j]);
+      if (j != i && d1 < d0 + d_span && d0 < d1 + d_span) return SP_ERR_INVALID_ARG;
+    }
+  }
+  return SP_OK;
+}
+
+extern "C" sp_status sp_pad_relayout_heads(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                                           int64_t B, int64_t T, int64_t T_pad, int32_t H, int32_t D,
+                                           sp_dtype dtype, int64_t src_batch_stride, sp_shard_strides head,
+                                           void* stream) {
+  if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
+  if (W < 1 || B < 0 || T < 0 || T_pad < T || H < 1 || D < 1) return SP_ERR_INVALID_ARG;
+  if (T_pad % W != 0) return SP_ERR_NOT_DIVISIBLE;
+  if (H % W != 0) return SP_ERR_INVALID_ARG;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t Hl = H / W, Ts = T_pad / W, run = Hl * D, row = int64_t(H) * D;
+  if ((run * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  if (src_batch_stride < T * row || (src_batch_stride * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  if (!disjoint_blocks(head.rank, head.batch, W, B, T_pad * run)) return SP_ERR_INVALID_ARG;
+  if (((head.rank | head.batch) * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  const int64_t s_span = B > 0 && T > 0 ? ((B - 1) * src_batch_stride + T * row) * eb : 0;
+  const int64_t d_span = B > 0 && T_pad > 0 ? ((W - 1) * head.rank + (B - 1) * head.batch + T_pad * run) * eb : 0;
+  const sp_status st = check_tensor_lists(src, dst, n_tensors, s_span, d_span);
+  if (st != SP_OK) return st;
+  if (B == 0 || Ts == 0) return SP_OK;
+  const int64_t V = run * eb / 16;
+  if (Ts * V >= (int64_t(1) << 32) - kChunk) return SP_ERR_UNSUPPORTED;
+  if (int64_t(W) * B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  RelayoutArgs a;
+  for (int i = 0; i < 3; ++i) {
+    a.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);
+    a.dst[i] = static_cast<char*>(dst[i < n_tensors ? i : 0]);
+  }
+  a.B = B;
+  a.tok_rank_b = Ts * row * eb;            // rank s's shard of the padded sequence
+  a.tok_batch_b = src_batch_stride * eb;
+  a.tok_row_b = row * eb;
+  a.head_rank_b = head.rank * eb;
+  a.head_batch_b = head.batch * eb;
+  a.run_b = run * eb;
+  a.seg_b = Ts * run * eb;
+  a.V = uint32_t(V);
+  a.fdV = make_fastdiv(uint32_t(V));
+  a.n_per_seg = uint32_t(Ts * V);
+  a.chunks = uint32_t(div_up(Ts * V, kChunk));
+  a.to_heads = 1;
+  a.Ts = Ts;
+  a.valid = T;
+  const int64_t gx = int64_t(a.chunks) * W;
+  if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  dim3 grid(unsigned(gx), unsigned(W * B), unsigned(n_tensors));
+  hipLaunchKernelGGL(relayout_kernel, grid, dim3(kThreads), 0, as_stream(stream), a);
+  return launch_status();
+}
+
+extern "C" sp_status sp_gather_heads_unpad(const void* const* src, void* const* dst, int32_t n_tensors, int32_t W,
+                                           int64_t B, int64_t T_pad, int32_t H, int32_t D, sp_dtype dtype,
+                                           sp_shard_strides head, const int64_t* counts, int64_t T, void* stream) {
+  if (!dtype_ok(dtype)) return SP_ERR_INVALID_ARG;
+  if (W < 1 || B < 0 || T_pad < 0 || T < 0 || H < 1 || D < 1) return SP_ERR_INVALID_ARG;
+  if (T_pad % W != 0) return SP_ERR_NOT_DIVISIBLE;
+  if (H % W != 0) return SP_ERR_INVALID_ARG;
+  if (W > kMaxWorldFused) return SP_ERR_UNSUPPORTED;
+  const int64_t eb = elem_bytes(dtype);
+  const int64_t Hl = H / W, Ts = T_pad / W, run = Hl * D, row = int64_t(H) * D;
+  if ((run * eb) % 16 != 0) return SP_ERR_UNSUPPORTED;
+  GatherHeadsUnpadArgs a;
+  a.cum[0] = 0;
+  for (int r = 0; r < W; ++r) {
+    const int64_t c = counts ? counts[r] : Ts;
+    if (c < 0 || c > Ts) return SP_ERR_INVALID_ARG;
+    a.cum[r + 1] = a.cum[r] + c;
+  }
+  if (a.cum[W] < T) return SP_ERR_INVALID_ARG;
+  if (!disjoint_blocks(head.rank, head.batch, W, B, T_pad * run)) return SP_ERR_INVALID_ARG;
+  if (((head.rank | head.batch) * eb) % 16 != 0) return SP_ERR_INVALID_ARG;
+  const int64_t s_span = B > 0 && T_pad > 0 ? ((W - 1) * head.rank + (B - 1) * head.batch + T_pad * run) * eb : 0;
+  const int64_t d_span = B * T * row * eb;
+  const sp_status st = check_tensor_lists(src, dst, n_tensors, s_span, d_span);
+  if (st != SP_OK) return st;
+  if (B == 0 || T == 0) return SP_OK;
+  const int64_t V = run * eb / 16;
+  if (Ts * V * W >= (int64_t(1) << 32) - kChunk) return SP_ERR_UNSUPPORTED;
+  if (B > kMaxGridY) return SP_ERR_UNSUPPORTED;
+  int64_t max_vec = 0;
+  for (int r = 0; r < W; ++r) {
+    int64_t kept = a.cum[r + 1] - a.cum[r];
+    if (a.cum[r] + kept > T) kept = T - a.cum[r];
+    if (kept < 0) kept = 0;
+    a.n_vec[r] = uint32_t(kept * W * V);
+    if (kept * W * V > max_vec) max_vec = kept * W * V;
+  }
+  for (int i = 0; i < 3; ++i) {
+    a.src[i] = static_cast<const char*>(src[i < n_tensors ? i : 0]);
+    a.dst[i] = static_cast<char*>(dst[i < n_tensors ? i : 0]);
+  }
+  a.head_rank_b = head.rank * eb;
+  a.head_batch_b = head.batch * eb;
+  a.run_b = run * eb;
+  a.seg_b = Ts * run * eb;
+  a.out_batch_b = T * row * eb;
+  a.row_b = row * eb;
+  a.V = uint32_t(V);
+  a.fdV = make_fastdiv(uint32_t(V));
+  a.fdRow = make_fastdiv(uint32_t(V * W));
+  a.chunks = uint32_t(div_up(max_vec, kChunk));
+  if (a.chunks == 0) return SP_OK;
+  const int64_t gx = int64_t(a.chunks) * W;
+  if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
+  hipLaunchKernelGGL(gather_heads_unpad_kernel, dim3(unsigned(gx), unsigned(B), unsigned(n_tensors)), dim3(kThreads), 0,
+                     as_stream(stream), a);
   return launch_status();
 }
 

@@ -101,10 +101,15 @@ class UlyssesStep:
             pairs = [(self.k, self.kp), (self.v, self.vp)]
         else:
             pairs = [(self.q, self.qp), (self.k, self.kp), (self.v, self.vp)]
-        for i, (x, y) in enumerate(pairs):
-            first = i == 0 and self.mask is not None
-            sp.sp_pad(x.view(wl.B, wl.T, C), y.view(wl.B, wl.T_pad, C), wl.T_pad,
-                      mask_in=self.mask if first else None, mask_out=self.mask_ext if first else None)
+        for x, y in pairs:
+            sp.sp_pad(x.view(wl.B, wl.T, C), y.view(wl.B, wl.T_pad, C), wl.T_pad)
+        self.pad_mask()
+
+    def pad_mask(self):
+        """The user mask's extension (补齐), in a call of its own: the mask may
+        be one (1, T, T) mask shared by every batch."""
+        if self.mask is not None and self.need_pad:
+            sp.sp_pad(None, None, self.wl.T_pad, mask_in=self.mask, mask_out=self.mask_ext)
 
     def partition(self):
         return sp.sp_partition(self.wl.T_pad, self.wl.W)
@@ -177,7 +182,43 @@ class UlyssesStep:
         else:
             sp.sp_gather_unpad(self.ot, self.out, wl.W, wl.B, self.Ts, C, wl.T, counts=lengths)
 
+    # -- the step with each pair of moves fused (the default) ------------------
+    # On one device pad followed by send_recv_heads is one permutation of the
+    # token rows (pad rows become zero runs on the head side), and so is
+    # gather_heads followed by gather_output_tokens: each pair is one library
+    # call that moves every byte once, with the same bytes as the two calls.
+    def pad_send(self):
+        wl = self.wl
+        C = wl.H * wl.D
+        if self.need_q_pad:
+            sp.sp_pad(self.q.view(wl.B, wl.Tq, C), self.qc.view(wl.B, wl.q_tokens_pad, C), wl.q_tokens_pad)
+        self.pad_mask()
+        if wl.cross:
+            src, dst = [self.k, self.v], [self.kh, self.vh]
+        else:
+            src, dst = [self.q, self.k, self.v], [self.qh, self.kh, self.vh]
+        sp.sp_pad_relayout_heads(src, dst, wl.W, wl.B, wl.T, wl.T_pad, wl.H, wl.D)
+
+    def gather_unpad(self, lengths):
+        wl = self.wl
+        if wl.cross:
+            sp.sp_gather_heads_unpad([self.oh], [self.out], wl.W, wl.B, wl.q_tokens_pad, wl.H, wl.D, wl.Tq,
+                                     counts=[self.Tsq] * wl.W)
+        else:
+            sp.sp_gather_heads_unpad([self.oh], [self.out], wl.W, wl.B, wl.T_pad, wl.H, wl.D, wl.T, counts=lengths)
+
     def run(self):
+        self.pad_send()
+        _, lengths = self.partition()
+        self.attention()
+        self.gather_unpad(lengths)
+        return self.out
+
+    def run_separate(self):
+        """The step as the five separate calls (pad, partition, send_recv_heads,
+        attention, gather_heads, gather_output_tokens): the same output bytes
+        as run(), with the padded token tensors and the token-side output
+        written along the way."""
         self.pad()
         _, lengths = self.partition()
         self.send_recv_heads()

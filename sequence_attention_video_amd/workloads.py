@@ -21,7 +21,7 @@ weights, prompts and latents that are not available here.  Recipe:
 from __future__ import annotations
 
 import math
-from dataclasses import dataclass
+from dataclasses import dataclass, replace
 
 import numpy as np
 
@@ -177,6 +177,22 @@ def block_causal_mask(t_valid: int, frames: int, frame_len: int, n_prompt: int) 
     k_prompt = (idx >= n_video)[None, :]
     vis = (k_frame <= q_frame) | k_prompt | q_prompt
     return vis.astype(np.uint8)[None]
+
+
+# Unit-spread variants of the video workloads: the same shapes and masks with
+# Q, K, V drawn N(0, 1) (seeds 1000 * index + 500 + {q: 0, k: 1, v: 2}).  With
+# N(0, 1/D) activations the scores q.k/sqrt(D) spread by about 1/D, every
+# softmax row is nearly uniform and outputs are about 1e-3, below the bf16
+# tolerance: a result that ignored the scores or the mask would pass.  With
+# unit-spread scores the softmax is far from uniform and such results miss the
+# tolerance by a wide margin.
+UNIT_SEED_OFFSET = 500
+UNIT_SPREAD = ("video_self", "uneven_mask", "long_hires")
+
+
+def unit_spread(wl: Workload) -> Workload:
+    """The workload with Q, K, V drawn N(0, 1) (see UNIT_SPREAD)."""
+    return replace(wl, std="1", name=wl.name + "_unit")
 
 
 def make_inputs(wl: Workload, seed_offset: int = 0) -> dict:

@@ -93,8 +93,10 @@ def test_validation_returns_before_launch(lib):
     z = A(0, 0, 0, 0)
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 96, b.SP_BF16, 64,
                                    None, 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+    # bf16 at D = 16 is supported (float32 MFMA on widened values): refused here
+    # only for its null tensors
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 16, b.SP_BF16, 64,
-                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_UNSUPPORTED
+                                   None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 128, b.SP_BF16, -1,
                                    None, 0, 0.1, None, 0, None) == b.SP_ERR_INVALID_ARG
     assert lib.sp_masked_attention(None, z, None, z, None, z, None, z, 1, 1, 64, 64, 1, 128, b.SP_BF16, 64,
@@ -130,6 +132,100 @@ def test_validation_returns_before_launch(lib):
     assert lib.sp_gather_unpad(None, S(0, 0), None, 2, 1, 3, 64, c, 6, b.SP_BF16, None) == b.SP_ERR_INVALID_ARG
     c = (ctypes.c_int64 * 2)(4, 2)
     assert lib.sp_gather_unpad(None, S(0, 0), None, 2, 1, 3, 64, c, 5, b.SP_BF16, None) == b.SP_ERR_INVALID_ARG
+
+
+def test_attention_scale_must_be_positive_and_normal(lib):
+    """The kernels hide a key with a -inf raw score and take the row maximum of
+    raw scores before scaling, so only a positive, finite, normal scale (and
+    scale * log2 e) is accepted; the rest are refused before any launch
+    (these fake pointers would fault if anything ran)."""
+    from sequence_attention_video_amd import binding as b
+    A = b.AttnStrides
+    qa, ka, va, oa = (ctypes.c_void_p(x << 40) for x in (1, 2, 3, 4))
+    st = A(0, 0, 512, 128)
+    for scale in (0.0, -0.0, -0.088, float("nan"), float("inf"), -float("inf"), 1e-40, 1e-45):
+        for dt, d in ((b.SP_BF16, 128), (b.SP_BF16, 64), (b.SP_F32, 16), (b.SP_BF16, 16)):
+            got = lib.sp_masked_attention(qa, st, ka, st, va, st, oa, st, 1, 1, 64, 64, 4, d, dt, 64,
+                                          None, 0, scale, None, 0, None)
+            assert got == b.SP_ERR_INVALID_ARG, (scale, dt, d, got)
+    with pytest.raises(ValueError):
+        b.check(lib.sp_masked_attention(qa, st, ka, st, va, st, oa, st, 1, 1, 64, 64, 4, 128, b.SP_BF16, 64,
+                                        None, 0, 0.0, None, 0, None))
+
+
+def test_pad_mask_alignment_and_shapes(lib):
+    """sp_pad reads the input mask as 4-byte words from its first byte on, so
+    a mask_in that is not 4-byte aligned is refused, as is a mask_out that is
+    not 16-byte aligned (host checks, no launch)."""
+    from sequence_attention_video_amd import binding as b
+    base_in, base_out = 1 << 40, 1 << 41
+    for off in (1, 2, 3):
+        assert lib.sp_pad(None, 0, None, 1, 6, 8, 0, b.SP_BF16, ctypes.c_void_p(base_in + off),
+                          ctypes.c_void_p(base_out), None) == b.SP_ERR_INVALID_ARG
+    assert lib.sp_pad(None, 0, None, 1, 6, 8, 0, b.SP_BF16, ctypes.c_void_p(base_in),
+                      ctypes.c_void_p(base_out + 4), None) == b.SP_ERR_INVALID_ARG
+    # the binding checks the mask shapes against B, T and T_pad before the call:
+    # a (1, T, T) mask shared by every batch is extended on its own, never
+    # with B > 1 token tensors
+    class FakeCuda:
+        def __init__(self, shape):
+            self.shape = shape
+            self.is_cuda = True
+
+        def is_contiguous(self):
+            return True
+
+    with pytest.raises(ValueError):
+        b.sp_pad(None, None, 8, mask_in=FakeCuda((1, 6, 6)), mask_out=FakeCuda((1, 8, 7)))
+    with pytest.raises(ValueError):
+        b.sp_pad(None, None, 8, mask_in=FakeCuda((1, 6, 6)), mask_out=None)
+
+
+def test_fused_moves_validation(lib):
+    """Argument checks of pad + send_recv_heads and gather_heads +
+    gather_output_tokens as single moves (all rejected, or nothing to move,
+    before any launch)."""
+    from sequence_attention_video_amd import binding as b
+    S = b.ShardStrides
+    vp = ctypes.c_void_p
+    src = (vp * 3)(vp(1 << 40), vp((1 << 40) + (1 << 32)), vp((1 << 40) + (2 << 32)))
+    dst = (vp * 3)(vp(1 << 41), vp((1 << 41) + (1 << 32)), vp((1 << 41) + (2 << 32)))
+    H, D, T, Tp, W = 32, 128, 6150, 6152, 8
+    hs = S(Tp * 4 * D, Tp * 4 * D)
+    pr = lib.sp_pad_relayout_heads
+    # T_pad not a multiple of W; T_pad < T; H not divisible by W
+    assert pr(src, dst, 3, W, 1, T, 6150, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_NOT_DIVISIBLE
+    assert pr(src, dst, 3, W, 1, T, 6144, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    assert pr(src, dst, 3, W, 1, T, Tp, 12, D, b.SP_BF16, T * 12 * D, hs, None) == b.SP_ERR_INVALID_ARG
+    # tensor count, null array, source batch stride below T*H*D, misaligned source
+    assert pr(src, dst, 4, W, 1, T, Tp, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    assert pr(None, dst, 3, W, 1, T, Tp, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    assert pr(src, dst, 3, W, 2, T, Tp, H, D, b.SP_BF16, T * H * D - 8, hs, None) == b.SP_ERR_INVALID_ARG
+    src_bad = (vp * 3)(vp((1 << 40) + 8), src[1], src[2])
+    assert pr(src_bad, dst, 3, W, 1, T, Tp, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    # a destination overlapping a source; head blocks overlapping each other
+    dst_bad = (vp * 3)(vp((1 << 40) + 4096), dst[1], dst[2])
+    assert pr(src, dst_bad, 3, W, 1, T, Tp, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_ERR_INVALID_ARG
+    assert pr(src, dst, 3, W, 2, T, Tp, H, D, b.SP_BF16, T * H * D, S(Tp * 4 * D, 100), None) == \
+        b.SP_ERR_INVALID_ARG
+    # a head group that is not whole 16-byte vectors; nothing to move
+    assert pr(src, dst, 1, W, 1, 50, 56, 8, 1, b.SP_F32, 50 * 8, S(56, 56), None) == b.SP_ERR_UNSUPPORTED
+    assert pr(src, dst, 3, W, 0, T, Tp, H, D, b.SP_BF16, T * H * D, hs, None) == b.SP_OK
+
+    gu = lib.sp_gather_heads_unpad
+    c = lambda *v: (ctypes.c_int64 * len(v))(*v)
+    assert gu(src, dst, 1, W, 1, 6150, H, D, b.SP_BF16, hs, None, T, None) == b.SP_ERR_NOT_DIVISIBLE
+    # a count above Ts; counts summing to less than T; W above 128 ranks
+    assert gu(src, dst, 1, W, 1, Tp, H, D, b.SP_BF16, hs, c(770, 769, 769, 769, 769, 769, 769, 769), T, None) == \
+        b.SP_ERR_INVALID_ARG
+    assert gu(src, dst, 1, W, 1, Tp, H, D, b.SP_BF16, hs, c(769, 769, 769, 769, 769, 769, 769, 766), T, None) == \
+        b.SP_ERR_INVALID_ARG
+    assert gu(src, dst, 1, 256, 1, 256 * 4, 256, 16, b.SP_BF16, S(1024 * 16, 1024 * 16), None, 1000, None) == \
+        b.SP_ERR_UNSUPPORTED
+    assert gu(None, dst, 1, W, 1, Tp, H, D, b.SP_BF16, hs, None, T, None) == b.SP_ERR_INVALID_ARG
+    dst_bad = (vp * 3)(vp((1 << 40) + 4096), dst[1], dst[2])
+    assert gu(src, dst_bad, 1, W, 1, Tp, H, D, b.SP_BF16, hs, None, T, None) == b.SP_ERR_INVALID_ARG
+    assert gu(src, dst, 1, W, 1, Tp, H, D, b.SP_BF16, hs, None, 0, None) == b.SP_OK
 
 
 def test_workspace_size(lib):

@@ -2,7 +2,8 @@
 point, bit-exact against the CPU oracle: sp_pad (tokens, in a separate and in
 the same buffer, and the user-mask extension), sp_relayout_heads both ways
 (one to three tensors), sp_gather_unpad with random per-rank counts, and
-sp_tile_2d_relayout_heads both ways.  Shapes cover W = 1..8, B = 1..3, ragged
+sp_tile_2d_relayout_heads both ways, and the fused moves (pad + send_recv_heads,
+gather_heads + gather_output_tokens).  Shapes cover W = 1..8, B = 1..3, ragged
 token counts, head groups of one to a few 16-byte vectors, fp32 and bf16.
 Outputs are prefilled with 0xFF bytes, so anything left unwritten (or written
 twice with other bytes) shows."""
@@ -117,3 +118,42 @@ def test_tile_2d_relayout_heads_random_shapes(i):
     for a, h, back in zip(xs, heads, backs):
         assert raw(h).tobytes() == O.send_recv_heads(O.split_cp_2d(a, F, Hh, Ww, sh, sw)).tobytes()
         assert raw(back).tobytes() == a.tobytes()
+
+
+@pytest.mark.parametrize("i", range(N_CASES))
+def test_fused_moves_random_shapes(i):
+    """pad + send_recv_heads and gather_heads + gather_output_tokens as single
+    moves: bit-exact against the oracle's composition of the two steps, one
+    to three tensors, a source batch stride above T*H*D, random trim counts."""
+    rng, dtype, W, B, Ts, Hl, D, T = case(100 + i)
+    H, T_pad = W * Hl, W * Ts
+    n = int(rng.integers(1, 4))
+    extra = int(rng.integers(0, 3)) * H * D               # rows of slack between batches of the source
+    say("fused moves shapes", i, dtype, W, B, Ts, Hl, D, T, n, extra)
+    xs = [bits(rng, (B, T * H * D + extra), dtype) for _ in range(n)]
+    heads = [sentinel_like((W, B, T_pad, Hl, D), TD[dtype]) for _ in range(n)]
+    srcs = [dev(a) for a in xs]
+    sp.sp_pad_relayout_heads([s[:, :T * H * D].view(B, T, H, D) if extra == 0 else s for s in srcs], heads,
+                             W, B, T, T_pad, H, D, src_batch_stride=T * H * D + extra)
+    torch.cuda.synchronize()
+    for a, h in zip(xs, heads):
+        x = a[:, :T * H * D].reshape(B, T, H, D)
+        want = O.send_recv_heads(O.token_shards(O.pad_tokens(x, T_pad), W))
+        assert raw(h).tobytes() == want.tobytes()
+    # the way back, with random per-rank counts that still cover T
+    hs = [bits(rng, (W, B, T_pad, Hl, D), dtype) for _ in range(n)]
+    counts = [int(c) for c in rng.integers(0, Ts + 1, size=W)]
+    short = T - sum(counts)
+    r = 0
+    while short > 0:
+        add = min(Ts - counts[r], short)
+        counts[r] += add
+        short -= add
+        r += 1
+    outs = [sentinel_like((B, T, H, D), TD[dtype]) for _ in range(n)]
+    sp.sp_gather_heads_unpad([dev(a) for a in hs], outs, W, B, T_pad, H, D, T, counts=counts)
+    torch.cuda.synchronize()
+    for a, o in zip(hs, outs):
+        tok = O.gather_heads(a)                                     # (W, B, Ts, H, D)
+        want = O.gather_output_tokens([tok[k].reshape(B, Ts, H * D) for k in range(W)], counts, T)
+        assert raw(o).reshape(B, T, H * D).tobytes() == want.tobytes()
