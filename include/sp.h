@@ -44,7 +44,8 @@ typedef enum {
   SP_ERR_NOT_DIVISIBLE = 1, /* a token count does not divide by the world size ([SP] 切分) */
   SP_ERR_INVALID_ARG = 2,   /* null pointer, bad size, bad stride, inconsistent counts */
   SP_ERR_UNSUPPORTED = 3,   /* valid request outside the built set (head dim, dtype) */
-  SP_ERR_HIP = 4            /* the HIP runtime refused a launch */
+  SP_ERR_HIP = 4,           /* the HIP runtime refused a launch */
+  SP_ERR_SCRATCH = 5        /* sp_masked_attention_noalloc: workspace beyond its fixed scratch */
 } sp_status;
 
 typedef enum { SP_F32 = 0, SP_BF16 = 1 } sp_dtype;
@@ -221,6 +222,35 @@ sp_status sp_masked_attention(const void* q, sp_attn_strides qs, const void* k, 
                               int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D, sp_dtype dtype,
                               int64_t kv_valid_len, const uint8_t* mask, int64_t mask_batch_stride, float scale,
                               void* workspace, size_t workspace_bytes, void* stream);
+
+/* Bytes of the fixed device scratch behind sp_masked_attention_noalloc. */
+#define SP_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+
+/*
+ * sp_masked_attention_noalloc -- sp_masked_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, result and errors as
+ * sp_masked_attention, without the workspace: the library uses a fixed
+ * scratch array of SP_NOALLOC_SCRATCH_BYTES in device memory, one per GPU,
+ * loaded with the library and held until the process ends.  The call makes
+ * no allocation and no free.  It uses exactly the workspace bytes that
+ * sp_masked_attention_workspace_size() reports for the same arguments, so
+ * its launches are the ones sp_masked_attention makes with a workspace of
+ * that size (the same bytes out).
+ * Every call on one GPU shares that GPU's scratch: calls that may overlap on
+ * one GPU (on different streams, or from several host threads) race on it
+ * and must be ordered by the caller.  Nothing in the scratch needs clearing
+ * between calls.
+ * Errors: those of sp_masked_attention; a call whose workspace size exceeds
+ * SP_NOALLOC_SCRATCH_BYTES (for example a user mask over very long
+ * sequences) -> SP_ERR_SCRATCH, with nothing launched; no HIP device ->
+ * SP_ERR_HIP.
+ */
+sp_status sp_masked_attention_noalloc(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
+                                      const void* v, sp_attn_strides vs, void* o, sp_attn_strides os, int32_t R,
+                                      int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D, sp_dtype dtype,
+                                      int64_t kv_valid_len, const uint8_t* mask, int64_t mask_batch_stride,
+                                      float scale, void* stream);
 
 /*
  * sp_gather_unpad -- gather_output_tokens ([SP] 还原).

@@ -17,7 +17,8 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libspattn.so")
 
-SP_OK, SP_ERR_NOT_DIVISIBLE, SP_ERR_INVALID_ARG, SP_ERR_UNSUPPORTED, SP_ERR_HIP = range(5)
+SP_OK, SP_ERR_NOT_DIVISIBLE, SP_ERR_INVALID_ARG, SP_ERR_UNSUPPORTED, SP_ERR_HIP, SP_ERR_SCRATCH = range(6)
+SP_NOALLOC_SCRATCH_BYTES = 128 * 1024 * 1024
 SP_F32, SP_BF16 = 0, 1
 SP_TOKENS_TO_HEADS, SP_HEADS_TO_TOKENS = 0, 1
 SP_GRID_TO_TILES, SP_TILES_TO_GRID = 0, 1
@@ -27,6 +28,7 @@ EXPORTS = (
     "sp_status_string", "sp_version", "sp_partition", "sp_pad", "sp_relayout_heads",
     "sp_masked_attention_workspace_size", "sp_masked_attention", "sp_gather_unpad", "sp_optimal_split",
     "sp_tile_2d", "sp_tile_2d_relayout_heads", "sp_pad_relayout_heads", "sp_gather_heads_unpad",
+    "sp_masked_attention_noalloc",
 )
 
 
@@ -69,6 +71,9 @@ def load(path: str | None = None) -> ctypes.CDLL:
     lib.sp_masked_attention.restype = ctypes.c_int
     lib.sp_masked_attention.argtypes = [vp, AttnStrides, vp, AttnStrides, vp, AttnStrides, vp, AttnStrides,
                                         i32, i64, i64, i64, i32, i32, ctypes.c_int, i64, vp, i64, f32, vp, sz, vp]
+    lib.sp_masked_attention_noalloc.restype = ctypes.c_int
+    lib.sp_masked_attention_noalloc.argtypes = [vp, AttnStrides, vp, AttnStrides, vp, AttnStrides, vp, AttnStrides,
+                                                i32, i64, i64, i64, i32, i32, ctypes.c_int, i64, vp, i64, f32, vp]
     lib.sp_gather_unpad.restype = ctypes.c_int
     lib.sp_gather_unpad.argtypes = [vp, ShardStrides, vp, i32, i64, i64, i64, ctypes.POINTER(i64), i64,
                                     ctypes.c_int, vp]
@@ -95,7 +100,7 @@ def check(status: int) -> None:
     if status == SP_OK:
         return
     msg = load().sp_status_string(status).decode()
-    if status in (SP_ERR_NOT_DIVISIBLE, SP_ERR_INVALID_ARG):
+    if status in (SP_ERR_NOT_DIVISIBLE, SP_ERR_INVALID_ARG, SP_ERR_SCRATCH):
         raise ValueError(msg)
     if status == SP_ERR_UNSUPPORTED:
         raise NotImplementedError(msg)
@@ -227,6 +232,28 @@ def sp_masked_attention(q, k, v, o, R: int, B: int, Tq: int, Tk: int, Hl: int, D
                                      int(R), int(B), int(Tq), int(Tk), int(Hl), int(D), dt, int(kv_valid_len),
                                      _ptr(mask), int(mbs), float(scale), _ptr(workspace), int(wbytes),
                                      _stream(stream)))
+
+
+def sp_masked_attention_noalloc(q, k, v, o, R: int, B: int, Tq: int, Tk: int, Hl: int, D: int,
+                                q_strides, k_strides, v_strides, o_strides, kv_valid_len: int | None = None,
+                                mask=None, mask_batch_stride: int | None = None, scale: float | None = None,
+                                stream=None):
+    """sp_masked_attention on the library's fixed per-GPU scratch: no workspace
+    argument and no allocation (calls on one GPU must not overlap)."""
+    _cuda(q, k, v, o, mask)
+    dt = _dtype_code(q)
+    if kv_valid_len is None:
+        kv_valid_len = Tk
+    if scale is None:
+        scale = 1.0 / (D ** 0.5)
+    mbs = 0
+    if mask is not None:
+        mbs = (mask.stride(0) if mask.shape[0] > 1 else 0) if mask_batch_stride is None else mask_batch_stride
+    check(load().sp_masked_attention_noalloc(_ptr(q), AttnStrides(*q_strides), _ptr(k), AttnStrides(*k_strides),
+                                             _ptr(v), AttnStrides(*v_strides), _ptr(o), AttnStrides(*o_strides),
+                                             int(R), int(B), int(Tq), int(Tk), int(Hl), int(D), dt,
+                                             int(kv_valid_len), _ptr(mask), int(mbs), float(scale),
+                                             _stream(stream)))
 
 
 def sp_gather_unpad(inp, out, W: int, B: int, Ts: int, C: int, T: int, counts=None,

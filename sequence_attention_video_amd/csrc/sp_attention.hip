@@ -50,6 +50,7 @@
 #include "sp_internal.h"
 
 #include <cmath>
+#include <mutex>
 #include <type_traits>
 
 namespace sp {
@@ -1259,4 +1260,65 @@ extern "C" sp_status sp_masked_attention(const void* q, sp_attn_strides qs, cons
                                   mask_batch_stride, scale, c);
   if (st != SP_OK || c.empty) return st;
   return attn_run(c, workspace, workspace_bytes, as_stream(stream));
+}
+
+// ---------------------------------------------------------------- no-allocation entry point
+
+// The workspace of sp_masked_attention_noalloc: a fixed array in device
+// memory, one per GPU (each device that loads the library holds its own copy
+// until the process ends).  In host code `scratch` names a host-side stand-in,
+// not device memory: its device address comes from hipGetSymbolAddress, taken
+// once per device with that device current, and only that address is ever
+// handed to a kernel.  Nothing in it needs to start at zero: the mask
+// classifier writes every class byte and visibility word a launch reads, and
+// a split launch writes every partial record its merge reads.
+static __device__ __align__(256) unsigned char scratch[SP_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch[kMaxDevices] = {};
+
+// Device address of the current device's scratch array.
+sp_status scratch_ptr(void** out) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) {
+    (void)hipGetLastError();
+    return SP_ERR_HIP;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return SP_ERR_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch[dev] == nullptr) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || p == nullptr) {
+      (void)hipGetLastError();
+      return SP_ERR_HIP;
+    }
+    g_scratch[dev] = p;
+  }
+  *out = g_scratch[dev];
+  return SP_OK;
+}
+}  // namespace
+
+extern "C" sp_status sp_masked_attention_noalloc(const void* q, sp_attn_strides qs, const void* k, sp_attn_strides ks,
+                                                 const void* v, sp_attn_strides vs, void* o, sp_attn_strides os,
+                                                 int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl, int32_t D,
+                                                 sp_dtype dtype, int64_t kv_valid_len, const uint8_t* mask,
+                                                 int64_t mask_batch_stride, float scale, void* stream) {
+  AttnCall c;
+  const sp_status st = attn_check(q, qs, k, ks, v, vs, o, os, R, B, Tq, Tk, Hl, D, dtype, kv_valid_len, mask,
+                                  mask_batch_stride, scale, c);
+  if (st != SP_OK || c.empty) return st;
+  // the same workspace as sp_masked_attention would be given (the size query's
+  // bytes), so both entry points take the same launch decisions
+  const size_t need = sp_masked_attention_workspace_size(R, B, Tq, Tk, Hl, D, dtype, mask != nullptr ? 1 : 0,
+                                                         mask_batch_stride);
+  if (need > size_t(SP_NOALLOC_SCRATCH_BYTES)) return SP_ERR_SCRATCH;
+  void* ws = nullptr;
+  if (need > 0) {
+    const sp_status sst = scratch_ptr(&ws);
+    if (sst != SP_OK) return sst;
+  }
+  return attn_run(c, ws, need, as_stream(stream));
 }

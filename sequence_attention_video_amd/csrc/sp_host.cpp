@@ -12,6 +12,9 @@ extern "C" const char* sp_status_string(sp_status status) {
     case SP_ERR_INVALID_ARG: return "SP_ERR_INVALID_ARG: invalid argument";
     case SP_ERR_UNSUPPORTED: return "SP_ERR_UNSUPPORTED: outside the supported set";
     case SP_ERR_HIP: return "SP_ERR_HIP: HIP runtime error at launch";
+    case SP_ERR_SCRATCH:
+      return "SP_ERR_SCRATCH: the call needs more workspace than the no-allocation entry point's fixed "
+             "scratch (SP_NOALLOC_SCRATCH_BYTES)";
   }
   return "SP_ERR_UNKNOWN";
 }

@@ -228,6 +228,33 @@ def test_fused_moves_validation(lib):
     assert gu(src, dst, 1, W, 1, Tp, H, D, b.SP_BF16, hs, None, 0, None) == b.SP_OK
 
 
+def test_noalloc_host_checks(lib):
+    """sp_masked_attention_noalloc checks its arguments like
+    sp_masked_attention, and refuses a request whose workspace exceeds its
+    fixed scratch with SP_ERR_SCRATCH, all before any HIP call (fake
+    pointers: anything launched would fault)."""
+    from sequence_attention_video_amd import binding as b
+    A = b.AttnStrides
+    qa, ka, va, oa, ma = (ctypes.c_void_p(x << 40) for x in (1, 2, 3, 4, 5))
+    st = A(0, 0, 512, 128)
+    na = lib.sp_masked_attention_noalloc
+    assert na(None, st, None, st, None, st, None, st, 1, 1, 64, 64, 4, 128, b.SP_BF16, 64, None, 0, 0.1,
+              None) == b.SP_ERR_INVALID_ARG
+    assert na(qa, st, ka, st, va, st, oa, st, 1, 1, 64, 64, 4, 96, b.SP_BF16, 64, None, 0, 0.1,
+              None) == b.SP_ERR_UNSUPPORTED
+    assert na(qa, st, ka, st, va, st, oa, st, 1, 1, 64, 64, 4, 128, b.SP_BF16, 64, None, 0, 0.0,
+              None) == b.SP_ERR_INVALID_ARG
+    assert na(qa, st, ka, st, va, st, oa, st, 1, 1, 0, 64, 4, 128, b.SP_BF16, 64, None, 0, 0.1, None) == b.SP_OK
+    T = 40000
+    s1 = A(0, 0, 128, 128)
+    assert lib.sp_masked_attention_workspace_size(1, 1, T, T, 1, 128, b.SP_BF16, 1, 0) > b.SP_NOALLOC_SCRATCH_BYTES
+    assert na(qa, s1, ka, s1, va, s1, oa, s1, 1, 1, T, T, 1, 128, b.SP_BF16, T, ma, 0, 0.088,
+              None) == b.SP_ERR_SCRATCH
+    assert lib.sp_status_string(b.SP_ERR_SCRATCH).startswith(b"SP_ERR_SCRATCH")
+    with pytest.raises(ValueError):
+        b.check(b.SP_ERR_SCRATCH)
+
+
 def test_workspace_size(lib):
     from sequence_attention_video_amd import binding as b
     # one class byte per (384-row, 64-key) tile of the mask (17 x 97 of them),
