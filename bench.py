@@ -1,15 +1,20 @@
 """Benchmark one step of the sequence-parallel attention path on one MI355X.
 
 A step is the whole path over one batch of synthetic input, all W virtual
-ranks per launch: pad -> partition -> send_recv_heads (Q, K, V in one launch)
--> masked attention on every rank's local heads -> gather_heads ->
-gather_output_tokens.  Inputs are resident in HBM before the timed region.
+ranks per launch: pad + send_recv_heads (Q, K, V in one launch, one move) ->
+partition -> masked attention on every rank's local heads -> gather_heads +
+gather_output_tokens (one move).  Inputs are resident in HBM before the timed
+region.  The default workload is long_hires (B = 2, 32768 tokens, the largest
+that the pages' long-sequence case describes); the others are available
+through --config.
 
 Prints one JSON line.  ``value`` is masked-attention TFLOP/s of the whole step
-(algorithmic attention flops per step / step time); the per-kernel figures,
-the attention roofline and the head-relayout bandwidth are added beside it.
+(algorithmic attention flops per step / step time); ``roofline`` is the
+all-ranks attention launch, ``roofline_share`` the launch of one rank's share
+alone (R = 1, what each GPU runs when the ranks are devices); the per-kernel
+figures and the head-relayout bandwidth are added beside them.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config video_self]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config long_hires]
 """
 
 from __future__ import annotations
@@ -386,7 +391,7 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first; the clocks need ~0.1 s of sustained work to settle")
-    ap.add_argument("--config", default="video_self")
+    ap.add_argument("--config", default="long_hires")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="budget of the oracle CPU baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--traffic-probe", action="store_true",
@@ -483,6 +488,11 @@ def main():
 
     # -- warmup, then K timed steps (events only around the K steps), then the
     #    same K steps again with per-stage events for the breakdown
+    run_bytes_in = (n_relayed * B * T * H * D * eb) + (n_relayed * B * Tp * H * D * eb)   # fused pad + send
+    if step.need_q_pad:
+        run_bytes_in += B * (wl.Tq + wl.q_tokens_pad) * H * D * eb
+    if step.need_pad and mask is not None:
+        run_bytes_in += mask.shape[0] * (T * T + Tp * Tp)
     log("warmup", args.warmup)
     for _ in range(args.warmup):
         step.run()
@@ -502,9 +512,29 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(4)] for _ in range(args.steps)]
     for i in range(args.steps):
         e = ev[i]
+        e[0].record(stream)
+        step.pad_send()
+        _, lengths = step.partition()
+        e[1].record(stream)
+        step.attention()
+        e[2].record(stream)
+        step.gather_unpad(lengths)
+        e[3].record(stream)
+    torch.cuda.synchronize()
+    # per-stage medians: a host stall inside one step's event pair (the GPU
+    # idles until the next launch arrives) would otherwise weigh in a mean
+    stage = lambda a, b: float(np.median([ev[i][a].elapsed_time(ev[i][b]) for i in range(args.steps)]))
+    ms_pad_send = stage(0, 1)
+    ms_attn_stage = stage(1, 2)
+    ms_gather_fused = stage(2, 3)
+    # the same step as the five separate calls (pad, send_recv_heads,
+    # attention, gather_heads, gather_output_tokens), stage by stage
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
+    for i in range(args.steps):
+        e = evs[i]
         e[0].record(stream)
         step.pad()
         _, lengths = step.partition()
@@ -517,13 +547,11 @@ def main():
         step.gather_output_tokens(lengths)
         e[4].record(stream)
     torch.cuda.synchronize()
-    # per-stage medians: a host stall inside one step's event pair (the GPU
-    # idles until the next launch arrives) would otherwise weigh in a mean
-    stage = lambda a, b: float(np.median([ev[i][a].elapsed_time(ev[i][b]) for i in range(args.steps)]))
-    ms_pad_send = stage(0, 1)
-    ms_attn_stage = stage(1, 2)
-    ms_gh = stage(2, 3)
-    ms_gather = stage(3, 4)
+    stage_s = lambda a, b: float(np.median([evs[i][a].elapsed_time(evs[i][b]) for i in range(args.steps)]))
+    ms_pad_send_sep = stage_s(0, 1)
+    ms_gh = stage_s(2, 3)
+    ms_gather = stage_s(3, 4)
+    ms_separate_step = float(np.median([evs[i][0].elapsed_time(evs[i][4]) for i in range(args.steps)]))
     # the dominant kernel's launch duration for the roofline: its in-step
     # median above; beside it, K launches back to back between one event pair
     # (the chip's clock runs lower under MFMA load with no copy in between)
@@ -537,7 +565,7 @@ def main():
     torch.cuda.synchronize()
     ms_attn_b2b = a0.elapsed_time(a1) / args.steps
     gc.enable()
-    per_step = [ev[i][0].elapsed_time(ev[i][4]) for i in range(args.steps)]
+    per_step = [ev[i][0].elapsed_time(ev[i][3]) for i in range(args.steps)]
     per_attn = [ev[i][1].elapsed_time(ev[i][2]) for i in range(args.steps)]
     spread = {"step_ms_median": round(float(np.median(per_step)), 4), "step_ms_min": round(float(np.min(per_step)), 4),
               "attention_ms_median": round(float(np.median(per_attn)), 4),
@@ -676,11 +704,24 @@ def main():
         return u
 
     tq_pad = wl.q_tokens_pad if wl.cross else Tp
+    t_out = wl.Tq if wl.cross else T
+    ts_q = tq_pad // W
+    # the two fused moves of the step, the same way
+    unpadded = (B, T, H, D)
+    fused_send_bytes = n_relayed * B * (T + Tp) * H * D * eb
+    ms_ps_rot, n_ps = rotating_ms(
+        lambda: ([rand_like(step.k.new_empty(unpadded)) for _ in range(n_relayed)],
+                 [torch.empty_like(step.kh) for _ in range(n_relayed)]),
+        lambda srcs, dsts: binding.sp_pad_relayout_heads(srcs, dsts, W, B, T, Tp, H, D),
+        fused_send_bytes)
+    ms_ghu_rot, n_ghu = rotating_ms(
+        lambda: (rand_like(step.oh), torch.empty_like(step.out)),
+        lambda src, dst: binding.sp_gather_heads_unpad([src], [dst], W, B, tq_pad, H, D, t_out, counts=[ts_q] * W),
+        gather_bytes)
     ms_gh_rot, n_gh = rotating_ms(
         lambda: (rand_like(step.oh), torch.empty_like(step.ot)),
         lambda src, dst: binding.sp_relayout_heads([src], [dst], W, B, tq_pad, H, D, binding.SP_HEADS_TO_TOKENS),
         relayout_o_bytes)
-    ts_q, t_out = tq_pad // W, (wl.Tq if wl.cross else T)
     ms_gather_rot, n_ga = rotating_ms(
         lambda: (rand_like(step.ot), torch.empty_like(step.out)),
         lambda src, dst: binding.sp_gather_unpad(src, dst, W, B, ts_q, H * D, t_out, counts=[ts_q] * W),
@@ -700,7 +741,7 @@ def main():
                                                            step.mask is not None, mbs)
     share_split = wl.dtype == "bf16" and need > mask_part
     share_ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
-    n_share = 5 if attn_flops > 4e12 else 50
+    n_share = 10 if attn_flops > 4e12 else max(20, args.steps)
     for _ in range(n_share):
         step.attention_rank(0, share_out, share_ws)
     s0 = torch.cuda.Event(enable_timing=True)
@@ -710,7 +751,16 @@ def main():
         step.attention_rank(0, share_out, share_ws)
     s1.record(stream)
     torch.cuda.synchronize()
-    ms_share = s0.elapsed_time(s1) / n_share
+    ms_share_b2b = s0.elapsed_time(s1) / n_share
+    # per-launch event pairs (the split launch's two kernels between one
+    # pair); the median is the share's launch time
+    sev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_share)]
+    for a_, b_ in sev:
+        a_.record(stream)
+        step.attention_rank(0, share_out, share_ws)
+        b_.record(stream)
+    torch.cuda.synchronize()
+    ms_share = float(np.median([a_.elapsed_time(b_) for a_, b_ in sev]))
     share_diff = float((share_out.float() - step.oh[0].float()).abs().max().item())
     share_flops = attn_flops // W
     share_tflops = share_flops / (ms_share * 1e-3) / 1e12
@@ -727,13 +777,39 @@ def main():
     peak_mfma = PEAK_BF16_TFLOPS if wl.dtype == "bf16" else PEAK_F32_MFMA_TFLOPS
     attn_tflops = attn_flops / (ms_attn * 1e-3) / 1e12
     traffic = read_traffic(wl.name, src_hash)
+    kname = ("attn_bf16_kernel<%d>" % D) if wl.dtype == "bf16" and D in (64, 128) else ("attn_f32_kernel<%d>" % D)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / peak_mfma, 4), "traffic": traffic,
-                "kernel": "attn_%s_kernel<%d>" % (wl.dtype, D), "flops_per_launch": attn_flops,
-                "avg_launch_ms": round(ms_attn, 4)}
+                "kernel": kname, "flops_per_launch": attn_flops,
+                "avg_launch_ms": round(ms_attn, 4), "R": W}
+    # one rank's share alone (R = 1): what each GPU runs when the ranks are
+    # devices; a split launch is the attention kernel plus the merge kernel
+    roofline_share = {"bound": "mfma", "achieved": round(share_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",
+                      "frac": round(share_tflops / peak_mfma, 4),
+                      "traffic": read_traffic(wl.name + "_share", src_hash),
+                      "kernel": kname + (" + attn_combine_kernel" if share_split else ""),
+                      "flops_per_launch": share_flops, "avg_launch_ms": round(ms_share, 4), "R": 1,
+                      "split": share_split}
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     kernels = {
-        "pad+send_recv_heads": {"ms": round(ms_pad_send, 4), "bytes": pad_bytes + relayout_bytes},
+        "pad+send_recv_heads": {"ms": round(ms_pad_send, 4), "bytes": run_bytes_in,
+                                "GB/s": round(gbs(run_bytes_in, ms_pad_send), 1),
+                                "note": "in the step: one fused move (plus the mask extension and the query pad "
+                                        "where the workload has them)"},
+        "gather_heads+gather_output_tokens": {"ms": round(ms_gather_fused, 4), "bytes": gather_bytes,
+                                              "GB/s": round(gbs(gather_bytes, ms_gather_fused), 1),
+                                              "note": "in the step: one fused move"},
+        "pad+send_recv_heads_fused_rotating": {"ms": round(ms_ps_rot, 4), "bytes": fused_send_bytes,
+                                               "GB/s": round(gbs(fused_send_bytes, ms_ps_rot), 1),
+                                               "hbm_frac": round(gbs(fused_send_bytes, ms_ps_rot) / PEAK_HBM_GBS, 4),
+                                               "buffer_sets": n_ps},
+        "gather_heads+gather_output_tokens_fused_rotating": {
+            "ms": round(ms_ghu_rot, 4), "bytes": gather_bytes, "GB/s": round(gbs(gather_bytes, ms_ghu_rot), 1),
+            "hbm_frac": round(gbs(gather_bytes, ms_ghu_rot) / PEAK_HBM_GBS, 4), "buffer_sets": n_ghu},
+        "separate_moves_step": {"ms": round(ms_separate_step, 4),
+                                "pad+send_recv_heads_ms": round(ms_pad_send_sep, 4),
+                                "bytes_pad+send": pad_bytes + relayout_bytes,
+                                "note": "the step as five separate calls (median of per-step event pairs)"},
         "send_recv_heads_rotating": {"ms": round(ms_relayout_rot, 4), "bytes": relayout_bytes,
                                      "GB/s": round(gbs(relayout_bytes, ms_relayout_rot), 1),
                                      "hbm_frac": round(gbs(relayout_bytes, ms_relayout_rot) / PEAK_HBM_GBS, 4),
@@ -762,7 +838,7 @@ def main():
         "step_spread": spread,
         "masked_attention_rank_share": {"ms": round(ms_share, 4), "TFLOP/s": round(share_tflops, 2),
                                         "mfma_frac": round(share_tflops / peak_mfma, 4), "R": 1,
-                                        "split": share_split,
+                                        "split": share_split, "back_to_back_ms": round(ms_share_b2b, 4),
                                         "max_abs_diff_vs_all_ranks": share_diff},
     }
 
@@ -787,6 +863,7 @@ def main():
         "config": {"workload": wl.name, "B": B, "T": T, "T_pad": Tp, "W": W, "H": H, "Hl": Hl, "D": D,
                    "mask": wl.mask, "cross": wl.cross, "Tq": wl.Tq if wl.cross else T},
         "roofline": roofline,
+        "roofline_share": roofline_share,
         "relayout": {"achieved": kernels["send_recv_heads_rotating"]["GB/s"], "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": kernels["send_recv_heads_rotating"]["hbm_frac"]},
         "cpu_baseline": cpu,

@@ -50,3 +50,33 @@ def rand_bits(rng, shape, dtype: str) -> np.ndarray:
     from sequence_attention_video_amd.workloads import f32_to_bf16_bits
     x = rng.standard_normal(shape).astype(np.float32)
     return f32_to_bf16_bits(x) if dtype == "bf16" else x
+
+
+def oracle_heads(q, k, v, scale, kv_valid, mask, rows=None, block=256):
+    """O.attention_heads(q, k, v, scale, kv_valid, mask, rows=rows)[:, rows]
+    computed by calling the oracle's per-head attention on (batch, head, row
+    block) pieces from a pool of threads, each with one BLAS thread (NumPy
+    releases the GIL in the oracle's array steps): the same function on the
+    same rows, spread over the host's cores.  q (B, Tq, Hh, D), k, v (B, Tk,
+    Hh, D) float64; mask (Bm, Tq, Tk) or None.  Returns (B, len(rows), Hh, D)."""
+    import os
+    from concurrent.futures import ThreadPoolExecutor
+
+    from threadpoolctl import threadpool_limits
+
+    import oracle as O
+    B, Tq, Hh, _ = q.shape
+    sel = np.arange(Tq) if rows is None else np.asarray(rows)
+    out = np.zeros((B, len(sel), Hh, v.shape[3]))
+    jobs = [(b, j, i0) for b in range(B) for j in range(Hh) for i0 in range(0, len(sel), block)]
+
+    def one(job):
+        b, j, i0 = job
+        r = sel[i0:i0 + block]
+        m = None if mask is None else mask[b if mask.shape[0] > 1 else 0][r]
+        out[b, i0:i0 + len(r), j] = O.attention(q[b, r, j], k[b, :, j], v[b, :, j], scale, kv_valid, m)
+
+    workers = max(1, min(16, len(os.sched_getaffinity(0))))
+    with threadpool_limits(limits=1), ThreadPoolExecutor(max_workers=workers) as ex:
+        list(ex.map(one, jobs))
+    return out

@@ -41,6 +41,12 @@ def test_bench_json_line():
     for key in ("bound", "achieved", "peak", "unit", "frac", "traffic"):
         assert key in r, key
     assert abs(r["frac"] - r["achieved"] / r["peak"]) < 1e-3
+    rs = d["roofline_share"]
+    for key in ("bound", "achieved", "peak", "unit", "frac", "traffic", "R", "flops_per_launch", "avg_launch_ms"):
+        assert key in rs, key
+    assert rs["R"] == 1 and abs(rs["frac"] - rs["achieved"] / rs["peak"]) < 1e-3
+    want_share = rs["flops_per_launch"] / (rs["avg_launch_ms"] * 1e-3) / 1e12
+    assert abs(rs["achieved"] - want_share) <= 0.01 * want_share + 0.006
     c = d["cpu_baseline"]
     for key in ("value", "unit", "cores", "kind", "sample"):
         assert key in c, key

@@ -36,7 +36,7 @@ import oracle as O
 from sequence_attention_video_amd.pipeline import UlyssesStep
 from sequence_attention_video_amd.workloads import (ORDER, UNIT_SEED_OFFSET, UNIT_SPREAD, WORKLOADS, make_inputs,
                                                     unit_spread)
-from tests.gpu_util import f64, raw, say, to_dev
+from tests.gpu_util import f64, oracle_heads, raw, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -173,14 +173,14 @@ def run_case(name, variant):
         kr, vr = f64(heads["k"][r]), f64(heads["v"][r])
         if wl.cross and Tq != wl.Tq:
             qr = O.pad_tokens(qr, Tq)
-        want = O.attention_heads(qr, kr, vr, scale, kv_valid, mask_ext, rows=rows)[:, rows]
+        want = oracle_heads(qr, kr, vr, scale, kv_valid, mask_ext, rows)
         want_oh[r] = want
         worst = max(worst, float(np.max(np.abs(ohf[r][:, rows] - want))))
         if discriminating(wl):
             zero_err = max(zero_err, float(np.max(np.abs(want))))
             uniform_err = max(uniform_err, float(np.max(np.abs(mean_of_visible(vr, kv_valid, mask_ext, rows) - want))))
             if mask_ext is not None:
-                ignore = O.attention_heads(qr[:, rows], kr, vr, scale, T, None)
+                ignore = oracle_heads(qr, kr, vr, scale, T, None, rows)
                 nomask_err = max(nomask_err, float(np.max(np.abs(ignore - want))))
     say("workload attention", wl.name, "max err", worst, "zero", zero_err, "uniform", uniform_err,
         "mask ignored", nomask_err)
@@ -257,8 +257,7 @@ def test_workload_rank_share(name, variant):
         assert np.isfinite(got).all()
         qr = f64(x["q"][:, :, r * Hl:(r + 1) * Hl]) if wl.cross else f64(heads["q"][r])
         rows = np.arange(Tq) if Tq <= FULL_ROWS_LIMIT else sampled_rows(Tq, Tq // W, rng, OTHER_RANK_ROWS)
-        want = O.attention_heads(qr, f64(heads["k"][r]), f64(heads["v"][r]), scale, kv_valid, mask_ext,
-                                 rows=rows)[:, rows]
+        want = oracle_heads(qr, f64(heads["k"][r]), f64(heads["v"][r]), scale, kv_valid, mask_ext, rows)
         err = float(np.max(np.abs(got[:, rows] - want)))
         say("rank share", wl.name, "rank", r, "max err", err)
         assert err <= TOL[wl.dtype], (r, err)
