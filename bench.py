@@ -64,9 +64,11 @@ def kernel_hash(*names) -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str, src_hash: str):
-    """HBM bytes per attention launch from the committed rocprofv3 counter summary,
-    if it was taken on the current kernel source; else None."""
+def read_traffic(workload: str, src_hash: str, key: str = "bytes_per_launch"):
+    """HBM bytes per attention launch (``key``: the all-ranks launch, or
+    "share_bytes_per_launch" for one rank's share) from the committed
+    rocprofv3 counter summary, if it was taken on the current kernel source;
+    else None."""
     path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
@@ -77,7 +79,7 @@ def read_traffic(workload: str, src_hash: str):
     rec = json.loads(m.group(1))
     if rec.get("kernel_source_hash") != src_hash:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get(key)
 
 
 COPY_PROBE_BYTES = 1 << 29   # plain device copy of known size for counter calibration
@@ -85,11 +87,13 @@ COPY_PROBE_BYTES = 1 << 29   # plain device copy of known size for counter calib
 
 def traffic_probe(workload: str, launches: int = 3):
     """Run only what the HBM counter passes measure: one plain copy of
-    COPY_PROBE_BYTES (calibration), then the step once and the attention
-    kernel `launches` more times."""
+    COPY_PROBE_BYTES (calibration), then the step once, the all-ranks
+    attention launch `launches` more times and rank 0's share alone (R = 1)
+    `launches` + 1 times."""
     import numpy as np
     import torch
 
+    from sequence_attention_video_amd import binding
     from sequence_attention_video_amd.pipeline import UlyssesStep
     from sequence_attention_video_amd.workloads import WORKLOADS, make_inputs
     wl = WORKLOADS[workload]
@@ -104,6 +108,13 @@ def traffic_probe(workload: str, launches: int = 3):
     step.run()
     for _ in range(launches):
         step.attention()
+    tq = wl.q_tokens_pad
+    need = binding.sp_masked_attention_workspace_size(1, wl.B, tq, wl.T_pad, wl.Hl, wl.D,
+                                                      binding._dtype_code(step.kh), step.mask is not None, 0)
+    ws = torch.empty(need, dtype=torch.uint8, device="cuda") if need else None
+    share_out = torch.empty_like(step.oh[0])
+    for _ in range(launches + 1):
+        step.attention_rank(0, share_out, ws)
     torch.cuda.synchronize()
     print("traffic probe done", workload, flush=True)
 
@@ -293,60 +304,84 @@ def _counter_rows(path):
 
 
 def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: list):
-    """Turn the two counter passes into profiles/attention_traffic_<workload>.md."""
+    """Turn the two counter passes over `bench.py --traffic-probe` into
+    profiles/attention_traffic_<workload>.md: bytes per launch of the
+    all-ranks attention launch, of one rank's share (the split launch and
+    its merge together), of the mask classifier and of the step's copy
+    kernels, each against the bytes the method must move."""
     import collections
+
+    from sequence_attention_video_amd.workloads import WORKLOADS
+    wl = WORKLOADS[workload]
     out = {}
     for name, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir)):
         per = collections.defaultdict(float)
-        kname = {}
+        kname, grid = {}, {}
         for r in _counter_rows(d):
             if r["Counter_Name"] != name:
                 continue
-            per[r["Dispatch_Id"]] += float(r["Counter_Value"])
-            kname[r["Dispatch_Id"]] = r["Kernel_Name"]
-        copy = [per[i] for i in per if "copy" in kname[i].lower() and "attn" not in kname[i]]
-        attn = [per[i] for i in per if "attn_bf16_kernel" in kname[i] or "attn_f32_kernel" in kname[i]]
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+            kname[int(r["Dispatch_Id"])] = r["Kernel_Name"]
+            grid[int(r["Dispatch_Id"])] = int(r["Grid_Size"])
+        ids = sorted(per)
+        copy = [per[i] for i in ids if "copyBuffer" in kname[i]]
         copy_kib = max(copy) if copy else float("nan")
         scale = (COPY_PROBE_BYTES / 1024.0) / copy_kib        # true KiB per counted KiB
-        first = lambda key: next((per[i] for i in sorted(per, key=int) if key in kname[i]), float("nan"))
+        is_attn = lambda i: "attn_bf16_kernel" in kname[i] or "attn_f32_kernel" in kname[i]
+        # the probe's first attention dispatch is the step's (all W shares);
+        # the share launches have another grid
+        g_all = next((grid[i] for i in ids if is_attn(i)), None)
+        all_ = [per[i] for i in ids if is_attn(i) and grid[i] == g_all]
+        share = [per[i] for i in ids if is_attn(i) and grid[i] != g_all]
+        comb = [per[i] for i in ids if "attn_combine_kernel" in kname[i]]
+        cls = [per[i] for i in ids if "classify_mask_kernel" in kname[i]]
+        avg = lambda v: sum(v) / len(v) if v else float("nan")
+        first = lambda key: next((per[i] for i in ids if key in kname[i]), float("nan"))
         out[name] = {"copy_kib": copy_kib, "scale": scale,
-                     "attention_kib": sum(attn[1:]) / max(1, len(attn[1:])) if len(attn) > 1 else (attn[0] if attn else float("nan")),
-                     "send_kib": first("relayout_kernel"), "gather_heads_kib": first("gather_heads_kernel"),
-                     "gather_unpad_kib": first("gather_unpad_kernel")}
-    fetch_b = out["FETCH_SIZE"]["attention_kib"] * out["FETCH_SIZE"]["scale"] * 1024
-    write_b = out["WRITE_SIZE"]["attention_kib"] * out["WRITE_SIZE"]["scale"] * 1024
+                     "all_kib": avg(all_[1:]) if len(all_) > 1 else avg(all_),
+                     "share_kib": avg(share[1:]) + (avg(comb[1:]) if len(comb) > 1 else 0.0),
+                     "classify_kib": avg(cls), "send_kib": first("relayout_kernel"),
+                     "pad_mask_kib": first("pad_mask_kernel"), "gather_kib": first("gather_heads_unpad_kernel")}
+    b = lambda ctr, key: out[ctr][key] * out[ctr]["scale"] * 1024
+    one = wl.B * wl.T_pad * wl.H * wl.D * wl.eb                 # one (B, T_pad, H, D) tensor
+    tq = wl.q_tokens_pad
+    q_o = 2 * wl.B * tq * wl.H * wl.D * wl.eb                    # Q read + O written
+    alg_all = q_o + 2 * one                                      # + K and V read once
     rec = {"workload": workload, "kernel_source_hash": kernel_hash("sp_attention.hip", "sp_internal.h"),
-           "bytes_per_launch": int(fetch_b + write_b), "fetch_bytes": int(fetch_b), "write_bytes": int(write_b),
+           "bytes_per_launch": int(b("FETCH_SIZE", "all_kib") + b("WRITE_SIZE", "all_kib")),
+           "fetch_bytes": int(b("FETCH_SIZE", "all_kib")), "write_bytes": int(b("WRITE_SIZE", "all_kib")),
+           "algorithmic_bytes": alg_all,
+           "share_bytes_per_launch": int(b("FETCH_SIZE", "share_kib") + b("WRITE_SIZE", "share_kib")),
+           "share_algorithmic_bytes": alg_all // wl.W,
            "fetch_scale": out["FETCH_SIZE"]["scale"], "write_scale": out["WRITE_SIZE"]["scale"]}
-    lines = [f"# HBM traffic of the attention kernel on {workload}", "",
+    lines = [f"# HBM traffic of the attention launches and the step's moves on {workload}", "",
              "Commands (run from the repository root on one MI355X):", "", "```"] + cmds + ["```", "",
              f"Calibration: a plain {COPY_PROBE_BYTES >> 20} MiB device copy read "
              f"{out['FETCH_SIZE']['copy_kib']:.0f} KiB (FETCH_SIZE) and wrote {out['WRITE_SIZE']['copy_kib']:.0f} KiB "
              f"(WRITE_SIZE) against {COPY_PROBE_BYTES >> 10} KiB moved, so the counters are scaled by "
-             f"{out['FETCH_SIZE']['scale']:.3f} and {out['WRITE_SIZE']['scale']:.3f}.", "",
-             "| counter | attention, KiB per launch (raw) | scaled bytes per launch |", "|---|---|---|",
-             f"| FETCH_SIZE | {out['FETCH_SIZE']['attention_kib']:.0f} | {fetch_b:.4g} |",
-             f"| WRITE_SIZE | {out['WRITE_SIZE']['attention_kib']:.0f} | {write_b:.4g} |", ""]
-    # the step's copy kernels (their first dispatch, inside the step): scaled
-    # counter bytes against the bytes the method must move
-    from sequence_attention_video_amd.workloads import WORKLOADS
-    wl = WORKLOADS[workload]
-    one = wl.B * wl.T_pad * wl.H * wl.D * wl.eb               # one (B, T_pad, H, D) tensor
+             f"{out['FETCH_SIZE']['scale']:.3f} and {out['WRITE_SIZE']['scale']:.3f}. Bytes below are scaled, per "
+             "launch (averages over the probe's launches of each kind after the first).", "",
+             "Algorithmic bytes of an attention launch: Q read, K and V read once, O written once (with a user "
+             "mask the launch also reads the classifier's visibility words).", "",
+             "| launch | fetched | written | total | algorithmic | total / algorithmic |", "|---|---|---|---|---|---|"]
+    def row(label, key, alg):
+        f_, w_ = b("FETCH_SIZE", key), b("WRITE_SIZE", key)
+        ratio = (f_ + w_) / alg if alg else float("nan")
+        lines.append(f"| {label} | {f_:.4g} | {w_:.4g} | {f_ + w_:.4g} | {alg:.4g} | {ratio:.3f} |")
+    row("attention, all W rank shares (R = W)", "all_kib", alg_all)
+    row("attention, rank 0's share alone (R = 1; a split launch's merge included)", "share_kib", alg_all // wl.W)
     nrel = 2 if wl.cross else 3
-    tq = wl.q_tokens_pad if wl.cross else wl.T_pad
-    alg = {"send_kib": (f"send_recv_heads (`relayout_kernel`, {nrel} tensors)", nrel * one, nrel * one),
-           "gather_heads_kib": ("gather_heads (`gather_heads_kernel`)", one * tq // wl.T_pad, one * tq // wl.T_pad),
-           "gather_unpad_kib": ("gather_output_tokens (`gather_unpad_kernel`)",
-                                wl.B * (wl.Tq if wl.cross else wl.T) * wl.H * wl.D * wl.eb,
-                                wl.B * (wl.Tq if wl.cross else wl.T) * wl.H * wl.D * wl.eb)}
-    lines += ["Copy kernels of the step (first dispatch of each; scaled counter bytes against the algorithmic "
-              "bytes read and written):", "",
-              "| kernel | fetched (scaled) | algorithmic read | written (scaled) | algorithmic write |",
-              "|---|---|---|---|---|"]
-    for key, (label, rd, wr) in alg.items():
-        f_b = out["FETCH_SIZE"][key] * out["FETCH_SIZE"]["scale"] * 1024
-        w_b = out["WRITE_SIZE"][key] * out["WRITE_SIZE"]["scale"] * 1024
-        lines.append(f"| {label} | {f_b:.4g} | {rd:.4g} | {w_b:.4g} | {wr:.4g} |")
+    send_alg = nrel * (wl.B * wl.T * wl.H * wl.D * wl.eb + one)
+    out_rows = wl.Tq if wl.cross else wl.T
+    gather_alg = 2 * wl.B * out_rows * wl.H * wl.D * wl.eb
+    row(f"pad + send_recv_heads, one move (`relayout_kernel`, {nrel} tensors)", "send_kib", send_alg)
+    row("gather_heads + gather_output_tokens, one move (`gather_heads_unpad_kernel`)", "gather_kib", gather_alg)
+    if wl.mask == "block_causal":
+        T, Tp = wl.T, wl.T_pad
+        row("user-mask extension (`pad_mask_kernel`)", "pad_mask_kib", T * T + Tp * Tp)
+        nkt = -(-Tp // 64)
+        row("mask classifier (`classify_mask_kernel`: mask read, classes and words written)", "classify_kib",
+            Tp * Tp + Tp * nkt * 8)
     lines += ["", "traffic_json: " + json.dumps(rec)]
     path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
@@ -354,30 +389,58 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
     print(open(path).read())
 
 
-def write_kernel_trace_summary(stats_csv: str, bench_json: str, title: str, cmd: str, out_name: str):
-    """Turn a rocprofv3 --stats kernel_stats.csv (and the bench line of the same
-    run) into a short markdown summary under profiles/."""
+def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd: str, out_name: str):
+    """Turn a rocprofv3 --kernel-trace kernel_trace.csv (and the bench line of
+    the same run) into a short markdown summary under profiles/.  Dispatches
+    are grouped by kernel and grid size, so that launches of one kernel with
+    different shapes (the all-ranks attention launch and one rank's share)
+    have averages of their own."""
+    import collections
     import csv
-    rows = list(csv.DictReader(open(stats_csv)))
+    import statistics
+    from sequence_attention_video_amd.workloads import WORKLOADS
     bench = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith('{"metric"')][-1])
+    wl = WORKLOADS[bench["config"]["workload"]]
+    groups = collections.defaultdict(list)
+    for r in csv.DictReader(open(trace_csv)):
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        groups[(r["Kernel_Name"], grid)].append(dur)
+    total = sum(sum(v) for v in groups.values())
+    is_attn = lambda name: "attn_bf16_kernel" in name or "attn_f32_kernel" in name
+    # the all-ranks launch is the attention grid launched most often; any
+    # other attention grid is rank 0's share alone
+    g_all = max(((g, len(v)) for (n, g), v in groups.items() if is_attn(n)), key=lambda t: t[1], default=(None, 0))[0]
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
-             "| kernel | calls | avg (us) | min (us) | max (us) | share |", "|---|---|---|---|---|---|"]
-    for r in rows:
-        name = r["Name"].replace("sp::(anonymous namespace)::", "")
-        name = name if len(name) <= 90 else name[:87] + "..."
-        lines.append(f"| `{name}` | {r['Calls']} | {float(r['AverageNs'])/1e3:.1f} | {float(r['MinNs'])/1e3:.1f} | "
-                     f"{float(r['MaxNs'])/1e3:.1f} | {float(r['Percentage']):.1f}% |")
-    k = bench["kernels"]
+             "Dispatches grouped by kernel and grid size (threads).", "",
+             "| kernel | grid | launch | calls | avg (us) | median (us) | min (us) | max (us) | share of time |",
+             "|---|---|---|---|---|---|---|---|---|"]
+    for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+        if sum(v) < 0.001 * total:
+            continue
+        short = name.replace("sp::(anonymous namespace)::", "")
+        short = short if len(short) <= 80 else short[:77] + "..."
+        kind = ("all ranks (R = %d)" % wl.W if grid == g_all else "one share (R = 1)") if is_attn(name) else (
+            "merge of the split share" if "attn_combine_kernel" in name else "")
+        lines.append(f"| `{short}` | {grid} | {kind} | {len(v)} | {sum(v) / len(v):.1f} | "
+                     f"{statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f} | {100 * sum(v) / total:.1f}% |")
+    r, rs, k = bench["roofline"], bench.get("roofline_share") or {}, bench["kernels"]
     lines += ["", "The same run's bench line (HIP events on the launch stream):", "",
-              f"* masked attention: {k['masked_attention']['ms']*1e3:.1f} us per launch, "
-              f"{k['masked_attention']['TFLOP/s']} TFLOP/s ({100*k['masked_attention']['mfma_frac']:.1f}% of the MFMA peak)",
-              f"* send_recv_heads (Q, K, V, rotating buffers): {k['send_recv_heads_rotating']['ms']*1e3:.1f} us, "
-              f"{k['send_recv_heads_rotating']['GB/s']} GB/s ({100*k['send_recv_heads_rotating']['hbm_frac']:.1f}% of 8000 GB/s)"]
-    for key, label in (("gather_heads_rotating", "gather_heads (O, rotating buffers)"),
-                       ("gather_output_tokens_rotating", "gather_output_tokens (rotating buffers)")):
+              f"* attention, all ranks: {r['avg_launch_ms'] * 1e3:.1f} us per launch (median in the step), "
+              f"{r['achieved']} TFLOP/s, {100 * r['frac']:.1f}% of the bf16 MFMA peak"]
+    if rs:
+        lines.append(f"* attention, one share (R = 1{', split + merge' if rs.get('split') else ''}): "
+                     f"{rs['avg_launch_ms'] * 1e3:.1f} us per launch, {rs['achieved']} TFLOP/s, "
+                     f"{100 * rs['frac']:.1f}% of the peak")
+    for key, label in (("send_recv_heads_rotating", "send_recv_heads (Q, K, V, rotating buffers)"),
+                       ("pad+send_recv_heads_fused_rotating", "pad + send_recv_heads, one move (rotating buffers)"),
+                       ("gather_heads+gather_output_tokens_fused_rotating",
+                        "gather_heads + gather_output_tokens, one move (rotating buffers)"),
+                       ("gather_heads_rotating", "gather_heads alone (rotating buffers)"),
+                       ("gather_output_tokens_rotating", "gather_output_tokens alone (rotating buffers)")):
         if key in k:
-            lines.append(f"* {label}: {k[key]['ms']*1e3:.1f} us, {k[key]['GB/s']} GB/s "
-                         f"({100*k[key]['hbm_frac']:.1f}% of 8000 GB/s)")
+            lines.append(f"* {label}: {k[key]['ms'] * 1e3:.1f} us, {k[key]['GB/s']} GB/s "
+                         f"({100 * k[key]['hbm_frac']:.1f}% of 8000 GB/s)")
     lines.append(f"* kernel source hash: `{bench['kernel_source_hash']}`")
     path = os.path.join(ROOT, "profiles", out_name)
     with open(path, "w", encoding="utf-8") as f:
@@ -404,8 +467,8 @@ def main():
                     help="write profiles/attention_mfma_<config>.md from one MFMA counter pass")
     ap.add_argument("--write-pipe-summary", metavar="PMC_DIR",
                     help="write profiles/attention_pipes_<config>.md from one issue-mix counter pass")
-    ap.add_argument("--write-kernel-trace-summary", nargs=2, metavar=("STATS_CSV", "BENCH_JSON"),
-                    help="write profiles/kernel_trace_<config>.md from a rocprofv3 --stats run of bench.py")
+    ap.add_argument("--write-kernel-trace-summary", nargs=2, metavar=("TRACE_CSV", "BENCH_JSON"),
+                    help="write profiles/kernel_trace_<config>.md from a rocprofv3 --kernel-trace run of bench.py")
     ap.add_argument("--profile-command", action="append", default=[],
                     help="the command line(s) that produced the profile, recorded in the summary")
     args = ap.parse_args()
@@ -786,7 +849,7 @@ def main():
     # devices; a split launch is the attention kernel plus the merge kernel
     roofline_share = {"bound": "mfma", "achieved": round(share_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                       "frac": round(share_tflops / peak_mfma, 4),
-                      "traffic": read_traffic(wl.name + "_share", src_hash),
+                      "traffic": read_traffic(wl.name, src_hash, "share_bytes_per_launch"),
                       "kernel": kname + (" + attn_combine_kernel" if share_split else ""),
                       "flops_per_launch": share_flops, "avg_launch_ms": round(ms_share, 4), "R": 1,
                       "split": share_split}
