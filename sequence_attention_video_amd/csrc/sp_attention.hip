@@ -121,7 +121,24 @@ struct AttnArgs {
   int64_t units;                         // items * nku
   int64_t upw;                           // units per workgroup (< nku)
   int32_t nku;                           // key tiles of KT per item
-  float* part;                           // partial records, two per workgroup
+  char* part;                            // partial records, two per workgroup (RecordLayout)
+};
+
+// One partial record of a split launch: for BM query rows, O/l of the
+// segment rounded once to bf16 (rows of D), then m (running max, log2 units)
+// and l (sum of p) per row in float32.  The merge recombines the segments'
+// O/l with weights 2^(m_s - M) l_s, so each record costs half the bytes of
+// unnormalised float32 rows; the one extra bf16 rounding of O/l adds at most
+// 2^-9 of |O/l| (a convex combination of V rows) to the result, below the
+// output's own bf16 rounding of the same size.
+template <int D>
+struct RecordLayout {
+  static constexpr int64_t BM = kRows<D>;
+  static constexpr int64_t kO = 0;                      // bf16 [BM][D]
+  static constexpr int64_t kM = BM * D * 2;             // float [BM]
+  static constexpr int64_t kL = kM + BM * 4;            // float [BM]
+  static constexpr int64_t kBytes = kL + BM * 4;
+  static_assert(kBytes % 256 == 0, "records stay 256-byte aligned");
 };
 
 // Workgroup i runs on XCD i % 8.  Give XCD x a contiguous range of logical
@@ -648,21 +665,25 @@ void attn_bf16_kernel(AttnArgs a) {
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
     if (!direct) {
-      // partial record: O rows (fp32, unnormalised), then m and l per row
+      // partial record: O/l rows (bf16), then m and l per row (float32)
+      using RL = RecordLayout<D>;
       const int row = 32 * QB * w + 32 * qb + l32;
-      float* rec = a.part + int64_t(2 * gl + (seg > 0 ? 1 : 0)) * (BM * (D + 2));
+      char* rec = a.part + int64_t(2 * gl + (seg > 0 ? 1 : 0)) * RL::kBytes;
       if (qvalid[qb]) {
+        const float inv = lt > 0.f ? 1.0f / lt : 0.f;
+        uint16_t* ro = reinterpret_cast<uint16_t*>(rec + RL::kO) + row * D;
 #pragma unroll
         for (int d = 0; d < NDB; ++d)
 #pragma unroll
           for (int g4 = 0; g4 < 4; ++g4) {
-            const f32x4 ov = {oacc[qb][d][4 * g4], oacc[qb][d][4 * g4 + 1], oacc[qb][d][4 * g4 + 2],
-                              oacc[qb][d][4 * g4 + 3]};
-            *reinterpret_cast<f32x4*>(rec + row * D + 32 * d + 8 * g4 + 4 * h) = ov;
+            bf16x4 ov;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) ov[i] = static_cast<__bf16>(oacc[qb][d][4 * g4 + i] * inv);
+            *reinterpret_cast<bf16x4*>(ro + 32 * d + 8 * g4 + 4 * h) = ov;
           }
         if (h == 0) {
-          rec[BM * D + row] = m_run[qb];
-          rec[BM * D + BM + row] = lt;
+          reinterpret_cast<float*>(rec + RL::kM)[row] = m_run[qb];
+          reinterpret_cast<float*>(rec + RL::kL)[row] = lt;
         }
       }
     } else {
@@ -687,16 +708,23 @@ void attn_bf16_kernel(AttnArgs a) {
 }
 
 // Merges the partial records of split launches: for every row of every item,
-// O = sum_s 2^(m_s - M) O_s / sum_s 2^(m_s - M) l_s with M = max_s m_s (the
-// same algebra as the running rescale, applied once), 0 where no key was
-// visible.  One workgroup per (item, 64 rows); 4 threads per row.
+// O = sum_s w_s (O/l)_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s
+// m_s (the running rescale's algebra, applied once), 0 where no key was
+// visible.  One workgroup per (item, 32 rows); kMergeTpr threads per row,
+// each D / kMergeTpr dims.  The records' m values are read first, then each
+// record's weight and O/l, their loads independent of the running sums.
+constexpr int kMergeTpr = 8;
+constexpr int kMergeRows = kThreads / kMergeTpr;   // rows per merge workgroup
+
 template <int D, bool MASK>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
+  using RL = RecordLayout<D>;
   constexpr int BM = kRows<D>;
-  constexpr int DPT = D / 4;   // dims per thread
+  constexpr int DPT = D / kMergeTpr;   // dims per thread (16 or 8: two or one 16-byte loads)
+  static_assert(DPT % 8 == 0, "whole 16-byte groups of bf16 per thread");
   const uint32_t item = blockIdx.x;
-  const int row = blockIdx.y * 64 + (threadIdx.x >> 2);
-  const int d0 = (threadIdx.x & 3) * DPT;
+  const int row = blockIdx.y * kMergeRows + int(threadIdx.x) / kMergeTpr;
+  const int d0 = (int(threadIdx.x) % kMergeTpr) * DPT;
   const TileCoord tc = decode_item<MASK>(a, item);
   const int64_t qrow = int64_t(tc.qt) * BM + row;
   if (qrow >= a.Tq) return;
@@ -705,23 +733,30 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const int64_t u0 = int64_t(item) * a.nku, u1 = u0 + a.nku;   // this item's units
   const int64_t g_first = u0 / a.upw, g_last = (u1 - 1) / a.upw;
   if (g_first == g_last) return;
-  float mx = -INFINITY;
-  for (int64_t g = g_first; g <= g_last; ++g) {
+  auto rec_of = [&](int64_t g) -> const char* {
     const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
-    mx = fmaxf(mx, a.part[slot * (BM * (D + 2)) + BM * D + row]);
-  }
+    return a.part + slot * RL::kBytes;
+  };
+  float mx = -INFINITY;
+  for (int64_t g = g_first; g <= g_last; ++g)
+    mx = fmaxf(mx, reinterpret_cast<const float*>(rec_of(g) + RL::kM)[row]);
   float acc[DPT] = {};
   float lsum = 0.f;
+#pragma unroll 4
   for (int64_t g = g_first; g <= g_last; ++g) {
-    const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
-    const float* rec = a.part + slot * (BM * (D + 2));
-    const float wgt = __builtin_amdgcn_exp2f(rec[BM * D + row] - mx);
-    lsum += wgt * rec[BM * D + BM + row];
+    const char* rec = rec_of(g);
+    const float wgt = __builtin_amdgcn_exp2f(reinterpret_cast<const float*>(rec + RL::kM)[row] - mx) *
+                      reinterpret_cast<const float*>(rec + RL::kL)[row];
+    lsum += wgt;
+    const uint16_t* ro = reinterpret_cast<const uint16_t*>(rec + RL::kO) + int64_t(row) * D + d0;
 #pragma unroll
-    for (int i = 0; i < DPT; i += 4) {
-      const f32x4 ov = *reinterpret_cast<const f32x4*>(rec + row * D + d0 + i);
+    for (int i = 0; i < DPT; i += 8) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(ro + i);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) acc[i + j] += wgt * ov[j];
+      for (int j = 0; j < 4; ++j) {
+        acc[i + 2 * j] += wgt * __uint_as_float(v[j] << 16);
+        acc[i + 2 * j + 1] += wgt * __uint_as_float(v[j] & 0xffff0000u);
+      }
     }
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
@@ -1017,7 +1052,7 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
       if (a.part) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
                            dim3(64 * kWaves<D>), 0, s, a);
-        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, kRows<D> / 64), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, kRows<D> / kMergeRows), dim3(kThreads), 0, s, a);
       } else {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(64 * kWaves<D>), 0, s, a);
       }
@@ -1089,7 +1124,9 @@ int64_t kernel_rows(sp_dtype dtype, int32_t D) { return bf16_mfma_kernel(dtype, 
 int64_t cls_rows(sp_dtype dtype, int32_t D) { return bf16_mfma_kernel(dtype, D) ? bf16_rows(D) : kClsRowsF32; }
 
 // bytes of partial records of a split launch: two slots per workgroup
-int64_t split_bytes(int64_t ncu, int32_t D) { return 2 * ncu * bf16_rows(D) * (int64_t(D) + 2) * 4; }
+int64_t split_bytes(int64_t ncu, int32_t D) {
+  return 2 * ncu * (D == 64 ? RecordLayout<64>::kBytes : RecordLayout<128>::kBytes);
+}
 
 // bytes of the class part of the workspace: one class byte per (class tile
 // rows x BN) tile, padded to 256 bytes
@@ -1233,7 +1270,7 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
     if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, c.D)) &&
         (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
       a.units = c.nwg * nku; a.upw = upw; a.nku = int32_t(nku);
-      a.part = reinterpret_cast<float*>(static_cast<char*>(workspace) + part_at);
+      a.part = static_cast<char*>(workspace) + part_at;
     }
   }
   if (c.has_mask) {

@@ -266,9 +266,11 @@ def test_workspace_size(lib):
     # Without a mask the workspace holds the partial records of split launches:
     # one rank's share of the 6144-token video workload (64 query tiles of 48
     # key tiles) splits over the 256 CUs (assumed when no GPU can be queried):
-    # two records of 384 rows x (128 + 2) floats per workgroup.
+    # two records per workgroup, each 384 rows of O/l in bf16 (128 values)
+    # and m, l in float32.
+    rec128 = 384 * (128 * 2 + 8)
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == \
-        2 * 256 * 384 * 130 * 4
+        2 * 256 * rec128
     # all eight shares fill the GPU evenly (512 query tiles, two per CU); the
     # cross share's 8 key tiles are too few to pay for the merge; the fp32
     # kernel never splits
@@ -279,7 +281,7 @@ def test_workspace_size(lib):
     # 105 tiles per CU split, so eight shares of the 6152-token workload split
     # when no user mask makes the tiles' costs uneven
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == \
-        2 * 256 * 384 * 130 * 4
+        2 * 256 * rec128
     # the long_hires share, 688 query tiles of 256 key tiles, would gain less
     # than the 1.3x the split asks for (three rounds unsplit, 688 + 4 tiles
     # per CU split)
