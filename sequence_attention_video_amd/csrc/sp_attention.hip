@@ -118,11 +118,20 @@ struct AttnArgs {
   float c;                               // scale * log2(e)
   uint32_t nwg;
   // split launches (bf16): the key tiles of all items in order
-  int64_t units;                         // items * nku
+  int64_t units;                         // items * nku (balanced split: unused, planned on the device)
   int64_t upw;                           // units per workgroup (< nku)
   int32_t nku;                           // key tiles of KT per item
   char* part;                            // partial records, two per workgroup (RecordLayout)
+  // balanced split of a masked launch (see attn_bf16_kernel): workgroups of
+  // the launch, and the plan written by logical workgroup 0 for the merge
+  int32_t split_wgs;
+  int32_t* plan_nnz;                     // non-empty key tiles of each query block, in dispatch order
+  int64_t* plan_s;                       // first unit of each query block; plan_s[nqt] = all units
+  int64_t* plan_start;                   // per logical workgroup: first unit, end unit, block, item << 32 | tile
 };
+
+// Query blocks a balanced split plans for (its per-block counts sit in LDS).
+constexpr int kMaxPlanBlocks = 512;
 
 // One partial record of a split launch: for BM query rows, O/l of the
 // segment rounded once to bf16 (rows of D), then m (running max, log2 units)
@@ -183,6 +192,16 @@ __device__ __forceinline__ TileCoord decode_item(const AttnArgs& a, uint32_t ite
   return t;
 }
 
+// A wave-uniform value moved to scalar registers (the compiler cannot tell
+// that values loaded from LDS or derived from them are uniform, and would
+// keep them in vector registers).
+__device__ __forceinline__ int32_t uniform(int32_t x) { return __builtin_amdgcn_readfirstlane(x); }
+__device__ __forceinline__ int64_t uniform(int64_t x) {
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x)));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(uint32_t(uint64_t(x) >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
 // max of x over the lane pair (l, l ^ 32): one v_permlane32_swap (no LDS trip)
 __device__ __forceinline__ float wave_max_pair(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
@@ -230,9 +249,10 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, bool MASK, bool SPLIT>
+template <int D, bool MASK, bool SPLIT, bool BAL = false>
 __global__ __launch_bounds__(64 * kWaves<D>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
 void attn_bf16_kernel(AttnArgs a) {
+  static_assert(!BAL || (MASK && SPLIT), "the balanced split is a split of masked launches");
   constexpr int WAVES = kWaves<D>, THREADS = 64 * WAVES, BM = kRows<D>;
   using T = Bf16Tile<D>;
   constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD, NG = T::NG;
@@ -278,12 +298,61 @@ void attn_bf16_kernel(AttnArgs a) {
   // partial, and each of those ends in a partial record (unnormalised O rows,
   // running max and sum) that attn_combine_kernel merges into O.
   const uint32_t gl = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0u;
-  int64_t u_next = SPLIT ? int64_t(gl) * a.upw : 0;
-  const int64_t u_end = SPLIT ? (a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
+  int64_t u_next = SPLIT && !BAL ? int64_t(gl) * a.upw : 0;
+  int64_t u_end = SPLIT && !BAL ? (a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
+  // Balanced split (masked launches whose items all share one mask): the
+  // units are the non-empty key tiles of every item, so each workgroup's
+  // range holds the same number of tiles that do work, where counting empty
+  // tiles too (above) leaves the ranges over long query tiles with several
+  // times the work of the others.  Items come query block by query block
+  // (block qi is query tile nqt-1-qi), (rank, batch, head) fastest, so every
+  // item of a block has the block's count of non-empty tiles
+  // (a.plan_nnz).  plan_balanced_split_kernel has written where this
+  // workgroup's range starts: block qi_cur, item p_cur of the block,
+  // non-empty tile k_cur of the item.  (Planned in a kernel of its own: the
+  // same planning inside this kernel pushed Q fragments out to scratch in
+  // the tile loop.)
+  int32_t qi_cur = 0, p_cur = 0, k_cur = 0;
+  const int32_t nrbh = int32_t(a.nwg / uint32_t(a.nqt));          // items per query block
+  const int32_t nku_b = int32_t((a.kv_end + KT - 1) / KT);          // key tiles below kv_end
+  if constexpr (BAL) {
+    const int64_t* st = a.plan_start + 4 * int64_t(gl);
+    u_next = uniform(st[0]);
+    u_end = uniform(st[1]);
+    qi_cur = int32_t(uniform(st[2]));
+    const int64_t pk = uniform(st[3]);
+    p_cur = int32_t(pk >> 32);
+    k_cur = int32_t(pk & 0xffffffff);
+  }
   for (int seg = 0;; ++seg) {
   uint32_t item;
   int kt_first = 0, kt_stop = 0;
-  if constexpr (SPLIT) {
+  int32_t k_first = 0, k_stop = 0, nnz_seg = 0;   // (BAL) this segment's non-empty tiles of its item
+  bool whole = false;                              // (BAL) the segment covers its whole item
+  if constexpr (BAL) {
+    if (u_next >= u_end) break;
+    while (uniform(a.plan_nnz[qi_cur]) == 0) {   // blocks with no visible key tile: the merge writes their zeros
+      ++qi_cur;
+      p_cur = 0;
+      k_cur = 0;
+    }
+    item = uint32_t(qi_cur * nrbh + p_cur);
+    nnz_seg = uniform(a.plan_nnz[qi_cur]);
+    k_first = k_cur;
+    k_stop = int64_t(nnz_seg - k_first) < u_end - u_next ? nnz_seg : k_first + int32_t(u_end - u_next);
+    whole = k_first == 0 && k_stop == nnz_seg;
+    u_next += k_stop - k_first;
+    if (k_stop == nnz_seg) {
+      k_cur = 0;
+      if (++p_cur == nrbh) {
+        p_cur = 0;
+        ++qi_cur;
+      }
+    } else {
+      k_cur = k_stop;
+    }
+    if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
+  } else if constexpr (SPLIT) {
     if (u_next >= u_end) break;
     item = uint32_t(u_next / a.nku);
     kt_first = int(u_next - int64_t(item) * a.nku);
@@ -342,6 +411,31 @@ void attn_bf16_kernel(AttnArgs a) {
       for (int i = tid; i < a.nkt + (a.nkt & 1); i += THREADS) cls_lds[i] = i < a.nkt ? cls_row[i] : uint8_t(kTileEmpty);
     }
     __syncthreads();
+  }
+  if constexpr (BAL) {
+    // key tile of the k-th non-empty key tile of this item's class row (nku_b
+    // when k is the count): each wave scans 64 tiles at a time with a ballot
+    auto nth_tile = [&](int32_t k) -> int {
+      for (int c0 = 0; c0 < nku_b; c0 += 64) {
+        const int kt = c0 + lane;
+        bool ne = false;
+        if (kt < nku_b) {
+          uint32_t c = cls_lds[2 * kt];
+          if (2 * kt + 1 < a.nkt) c |= cls_lds[2 * kt + 1];
+          ne = c != kTileEmpty;
+        }
+        const uint64_t m = __ballot(ne);
+        const int cnt = __popcll(m);
+        if (k < cnt) {
+          const uint32_t below = __builtin_amdgcn_mbcnt_hi(uint32_t(m >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(m), 0u));
+          return c0 + __ffsll((unsigned long long)__ballot(ne && int(below) == k)) - 1;
+        }
+        k -= cnt;
+      }
+      return nku_b;
+    };
+    kt_first = uniform(nth_tile(k_first));
+    kt_stop = k_stop == nnz_seg ? nku_b : uniform(nth_tile(k_stop));
   }
   // Key tiles of KT keys; with a user mask a tile's class combines the classes
   // of its BN-key class tiles, and empty tiles are skipped.  This segment runs
@@ -660,7 +754,7 @@ void attn_bf16_kernel(AttnArgs a) {
   // A segment that covers its whole item writes O; a partial one (split
   // launches) writes a record, in slot 2*g if it is the workgroup's first
   // segment, else (it is then the last) in slot 2*g + 1.
-  const bool direct = !SPLIT || (kt_first == 0 && kt_stop == a.nku);
+  const bool direct = !SPLIT || (BAL ? whole : kt_first == 0 && kt_stop == a.nku);
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float lt = l_run[qb] + __shfl_xor(l_run[qb], 32);
@@ -716,7 +810,7 @@ void attn_bf16_kernel(AttnArgs a) {
 constexpr int kMergeTpr = 8;
 constexpr int kMergeRows = kThreads / kMergeTpr;   // rows per merge workgroup
 
-template <int D, bool MASK>
+template <int D, bool MASK, bool BAL = false>
 __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   using RL = RecordLayout<D>;
   constexpr int BM = kRows<D>;
@@ -728,13 +822,35 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   const TileCoord tc = decode_item<MASK>(a, item);
   const int64_t qrow = int64_t(tc.qt) * BM + row;
   if (qrow >= a.Tq) return;
-  // workgroups whose unit ranges meet this item, and the slot of each; an
-  // item inside one range was written whole by its workgroup
-  const int64_t u0 = int64_t(item) * a.nku, u1 = u0 + a.nku;   // this item's units
-  const int64_t g_first = u0 / a.upw, g_last = (u1 - 1) / a.upw;
+  uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3] + qrow * a.os[2];
+  // this item's units [u0, u1) and the units per workgroup; workgroups whose
+  // unit ranges meet the item, and the slot of each; an item inside one
+  // range was written whole by its workgroup
+  int64_t u0, u1, upw;
+  if constexpr (BAL) {
+    // the balanced split's plan: an item of query block qi has plan_nnz[qi]
+    // units; a block without any visible key tile was run by no workgroup,
+    // and its rows are 0
+    const int32_t nrbh = int32_t(a.nwg / uint32_t(a.nqt));
+    const int32_t qi = int32_t(item) / nrbh;
+    const int32_t n = a.plan_nnz[qi];
+    if (n == 0) {
+#pragma unroll
+      for (int i = 0; i < DPT; i += 4) *reinterpret_cast<bf16x4*>(orow + d0 + i) = bf16x4{};
+      return;
+    }
+    u0 = a.plan_s[qi] + int64_t(int32_t(item) - qi * nrbh) * n;
+    u1 = u0 + n;
+    upw = (a.plan_s[a.nqt] + a.split_wgs - 1) / a.split_wgs;
+  } else {
+    u0 = int64_t(item) * a.nku;
+    u1 = u0 + a.nku;
+    upw = a.upw;
+  }
+  const int64_t g_first = u0 / upw, g_last = (u1 - 1) / upw;
   if (g_first == g_last) return;
   auto rec_of = [&](int64_t g) -> const char* {
-    const int64_t slot = 2 * g + (g * a.upw < u0 ? 1 : 0);
+    const int64_t slot = 2 * g + (g * upw < u0 ? 1 : 0);
     return a.part + slot * RL::kBytes;
   };
   float mx = -INFINITY;
@@ -760,7 +876,6 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
     }
   }
   const float inv = lsum > 0.f ? 1.0f / lsum : 0.f;
-  uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.r * a.os[0] + tc.b * a.os[1] + tc.head * a.os[3] + qrow * a.os[2];
 #pragma unroll
   for (int i = 0; i < DPT; i += 4) {
     bf16x4 ov;
@@ -938,6 +1053,73 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
   }
 }
 
+// ---------------------------------------------------------------- balanced split plan
+
+// Plans a balanced split (see attn_bf16_kernel) from the class map of the
+// one mask every item shares: per query block (dispatch order, block qi =
+// query tile nqt-1-qi) the count of non-empty key tiles below kv_end, their
+// prefix sums over the items, and for each of the split_wgs logical
+// workgroups its range of units [u, u_end) with the block, the item of the
+// block and the non-empty tile of the item that unit u falls on.  One
+// workgroup; nqt <= kMaxPlanBlocks <= its threads.
+constexpr int kPlanThreads = 512;
+static_assert(kMaxPlanBlocks <= kPlanThreads, "one query block per thread in the prefix sum");
+
+__global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnArgs a) {
+  __shared__ int32_t nnz[kMaxPlanBlocks];
+  __shared__ int64_t pre[kMaxPlanBlocks];   // inclusive prefix sums of units over the blocks
+  const int tid = threadIdx.x;
+  const int32_t nqt = a.nqt;
+  const int32_t nrbh = int32_t(a.nwg / uint32_t(nqt));
+  const int32_t nku = int32_t((a.kv_end + KT - 1) / KT);
+  for (int i = tid; i < nqt; i += kPlanThreads) nnz[i] = 0;
+  __syncthreads();
+  for (int i = tid; i < nqt * nku; i += kPlanThreads) {
+    const int qi = i / nku, j = i - qi * nku;
+    const uint8_t* row = a.cls + int64_t(nqt - 1 - qi) * a.nkt;
+    uint32_t c = row[2 * j];
+    if (2 * j + 1 < a.nkt) c |= row[2 * j + 1];
+    if (c != kTileEmpty) atomicAdd(&nnz[qi], 1);
+  }
+  __syncthreads();
+  if (tid < nqt) pre[tid] = int64_t(nnz[tid]) * nrbh;
+  __syncthreads();
+  for (int off = 1; off < nqt; off *= 2) {
+    const int64_t add = tid < nqt && tid >= off ? pre[tid - off] : 0;
+    __syncthreads();
+    if (tid < nqt) pre[tid] += add;
+    __syncthreads();
+  }
+  const int64_t total = pre[nqt - 1];
+  for (int i = tid; i < nqt; i += kPlanThreads) {
+    a.plan_nnz[i] = nnz[i];
+    a.plan_s[i] = i == 0 ? 0 : pre[i - 1];
+  }
+  if (tid == 0) a.plan_s[nqt] = total;
+  const int64_t upw = (total + a.split_wgs - 1) / a.split_wgs;
+  for (int g = tid; g < a.split_wgs; g += kPlanThreads) {
+    const int64_t u = int64_t(g) * upw;
+    const int64_t u_end = total < u + upw ? total : u + upw;
+    int64_t* st = a.plan_start + 4 * int64_t(g);
+    st[0] = u;
+    st[1] = u_end;
+    st[2] = 0;
+    st[3] = 0;
+    if (u >= u_end) continue;
+    // the first block whose inclusive sum exceeds u (it has units, so u lies
+    // inside one of its items)
+    int lo = 0, hi = nqt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (pre[mid] > u) hi = mid; else lo = mid + 1;
+    }
+    const int64_t within = u - (lo == 0 ? 0 : pre[lo - 1]);
+    const int64_t p = within / nnz[lo], k = within - p * nnz[lo];
+    st[2] = lo;
+    st[3] = (p << 32) | k;
+  }
+}
+
 // ---------------------------------------------------------------- mask tiles
 
 // One workgroup (16 waves) per (batch, block of `rows` mask rows, kClsSpan
@@ -1049,7 +1231,15 @@ template <int D, bool MASK>
 void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
   if (bf16_mfma_kernel(dt, D)) {
     if constexpr (D % 32 == 0) {
-      if (a.part) {
+      if (a.part && a.split_wgs > 0) {
+        if constexpr (MASK && D == 128) {
+          hipLaunchKernelGGL(plan_balanced_split_kernel, dim3(1), dim3(kPlanThreads), 0, s, a);
+          hipLaunchKernelGGL((attn_bf16_kernel<D, true, true, true>), dim3(unsigned(a.split_wgs)),
+                             dim3(64 * kWaves<D>), 0, s, a);
+          hipLaunchKernelGGL((attn_combine_kernel<D, true, true>), dim3(a.nwg, kRows<D> / kMergeRows), dim3(kThreads),
+                             0, s, a);
+        }
+      } else if (a.part) {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
                            dim3(64 * kWaves<D>), 0, s, a);
         hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, kRows<D> / kMergeRows), dim3(kThreads), 0, s, a);
@@ -1143,19 +1333,36 @@ int64_t mask_ws_bytes(int64_t B, int64_t Tq, int64_t Tk, bool has_mask, int64_t 
   return cls_ws_bytes(bm, Tq, Tk, rows) + bm * div_up(Tq, 2) * 2 * div_up(Tk, BN) * 8;
 }
 
+// A masked split launch cuts its ranges in non-empty key tiles (the balanced
+// split) when the kernel can plan them: D = 128, one mask for every batch (or
+// one batch), at most kMaxPlanBlocks query blocks.
+bool balanced_split(bool has_mask, int32_t D, int64_t mask_batch_stride, int64_t B, int64_t nqt) {
+  return has_mask && D == 128 && (mask_batch_stride == 0 || B == 1) && nqt <= kMaxPlanBlocks;
+}
+
+// The balanced split's plan: prefix sums (nqt + 1 int64), counts (nqt int32),
+// then four int64 per workgroup (its start); 256-byte aligned in all.
+int64_t plan_counts_at(int64_t nqt) { return (nqt + 1) * 8; }
+int64_t plan_starts_at(int64_t nqt) { return (plan_counts_at(nqt) + nqt * 4 + 7) / 8 * 8; }
+int64_t plan_bytes(int64_t nqt, int64_t wgs) { return (plan_starts_at(nqt) + wgs * 32 + 255) / 256 * 256; }
+
 extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64_t Tq, int64_t Tk, int32_t Hl,
                                                      int32_t D, sp_dtype dtype, int32_t has_mask,
                                                      int64_t mask_batch_stride) {
   if (R <= 0 || B <= 0 || Tq <= 0 || Tk <= 0 || Hl <= 0) return 0;
-  // [mask classes and words][partial records of a split launch, 256-byte
-  // aligned]; the split part is sized for kv_valid_len = Tk (a shorter key
-  // range needs no more)
+  // [mask classes and words][a balanced split's plan][partial records of a
+  // split launch], each part 256-byte aligned; the split part is sized for
+  // kv_valid_len = Tk (a shorter key range needs no more)
   const int64_t mask_bytes = mask_ws_bytes(B, Tq, Tk, has_mask != 0, mask_batch_stride, cls_rows(dtype, D));
   int64_t split = 0;
   if (bf16_mfma_kernel(dtype, D)) {
     const int64_t ncu = device_cus();
-    const int64_t items = div_up(Tq, bf16_rows(D)) * Hl * B * R;
-    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D, has_mask != 0)) split = split_bytes(ncu, D);
+    const int64_t nqt = div_up(Tq, bf16_rows(D));
+    const int64_t items = nqt * Hl * B * R;
+    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D, has_mask != 0)) {
+      split = split_bytes(ncu, D);
+      if (balanced_split(has_mask != 0, D, mask_batch_stride, B, nqt)) split += plan_bytes(nqt, ncu);
+    }
   }
   return size_t(split ? (mask_bytes + 255) / 256 * 256 + split : mask_bytes);
 }
@@ -1236,6 +1443,7 @@ sp_status attn_check(const void* q, sp_attn_strides qs, const void* k, sp_attn_s
   a.c = c2;
   a.nwg = uint32_t(nwg);
   a.units = 0; a.upw = 0; a.nku = 0; a.part = nullptr;
+  a.split_wgs = 0; a.plan_nnz = nullptr; a.plan_s = nullptr; a.plan_start = nullptr;
   c.dtype = dtype;
   c.D = D;
   c.has_mask = has_mask;
@@ -1266,11 +1474,21 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
     // the split runs only with room for its partial records after the mask
     // part (as sized by sp_masked_attention_workspace_size); otherwise the
     // plain launch runs
-    const int64_t part_at = (c.mask_bytes + 255) / 256 * 256;
+    const bool bal = balanced_split(c.has_mask, c.D, a.mask_bs, a.B, a.nqt);
+    const int64_t plan_at = (c.mask_bytes + 255) / 256 * 256;
+    const int64_t part_at = plan_at + (bal ? plan_bytes(a.nqt, ncu) : 0);
     if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, c.D)) &&
         (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
       a.units = c.nwg * nku; a.upw = upw; a.nku = int32_t(nku);
       a.part = static_cast<char*>(workspace) + part_at;
+      if (bal) {
+        // one range of non-empty key tiles per compute unit, planned on the device
+        a.split_wgs = int32_t(ncu);
+        char* plan = static_cast<char*>(workspace) + plan_at;
+        a.plan_s = reinterpret_cast<int64_t*>(plan);
+        a.plan_nnz = reinterpret_cast<int32_t*>(plan + plan_counts_at(a.nqt));
+        a.plan_start = reinterpret_cast<int64_t*>(plan + plan_starts_at(a.nqt));
+      }
     }
   }
   if (c.has_mask) {

@@ -3,10 +3,10 @@ video->audio and audio->video cross-attention, each modality padded to its own
 multiple of W) at full size on the GPU, against the CPU oracle:
 
 * the audio query modality's padding (987 -> 992 rows) bit-exact;
-* every part's final output on sampled query rows (first, last, shard
-  boundaries, the last real row) within 2e-2 of unsharded float64 attention
-  on the real tokens (the sharded == unsharded invariant);
-* the zero-copy form of every part byte-identical to its exchange path;
+* every part's final output on every query row within 2e-2 of unsharded
+  float64 attention on the real tokens (the sharded == unsharded invariant);
+* the zero-copy form of every part byte-identical to its exchange path, and
+  against the same oracle rows directly;
 * the four parts run concurrently on their own streams give the same bytes
   as run one after another, on several steps in a row.
 """
@@ -20,19 +20,11 @@ import torch
 import oracle as O
 from sequence_attention_video_amd.pipeline import JointAVStep
 from sequence_attention_video_amd.workloads import JOINT_AV, make_joint_inputs
-from tests.gpu_util import f64, raw, say
+from tests.gpu_util import f64, oracle_heads, raw, say
 
 pytestmark = pytest.mark.gpu
 
 TOL = 2e-2
-
-
-def sample_rows(n, shard, rng):
-    rows = {0, 1, n - 1, n - 2}
-    for s in range(1, max(1, n // shard)):
-        rows.update({s * shard - 1, s * shard})
-    rows.update(int(x) for x in rng.integers(0, n, 6))
-    return np.array(sorted(r for r in rows if 0 <= r < n))
 
 
 def test_joint_av_block():
@@ -42,7 +34,6 @@ def test_joint_av_block():
     step = JointAVStep(jw, x)
     outs = step.run()
     torch.cuda.synchronize()
-    rng = np.random.default_rng(6)
     parts = jw.parts()
     # the audio queries of the audio->video cross-attention, padded on their own
     a2v = step.steps["a2v"]
@@ -54,23 +45,34 @@ def test_joint_av_block():
         tq = wl.q_tokens
         assert got.shape == (wl.B, tq, wl.H, wl.D)
         assert np.isfinite(got).all()
-        rows = sample_rows(tq, wl.q_tokens_pad // wl.W, rng)
-        q = f64(x[name]["q"])[:, rows]
-        want = O.attention_heads(q, f64(x[name]["k"]), f64(x[name]["v"]), 1.0 / math.sqrt(wl.D), wl.T, None)
-        err = np.max(np.abs(got[:, rows] - want))
+        want = oracle_heads(f64(x[name]["q"]), f64(x[name]["k"]), f64(x[name]["v"]), 1.0 / math.sqrt(wl.D), wl.T,
+                            None)
+        err = np.max(np.abs(got - want))
         assert err <= TOL, (name, err)
 
 
-def test_joint_av_zero_copy_matches_exchange_path():
+def test_joint_av_zero_copy_matches_exchange_path_and_oracle():
+    """The zero-copy form of each part (both exchanges folded into
+    attention's strides): byte-identical to the exchange path, and on every
+    query row within the tolerance of unsharded float64 attention."""
     say("joint_av zero-copy")
     jw = JOINT_AV
-    step = JointAVStep(jw, make_joint_inputs(jw))
+    x = make_joint_inputs(jw)
+    step = JointAVStep(jw, x)
+    parts = jw.parts()
     for name in JointAVStep.PARTS:
         s = step.steps[name]
         out = s.run().clone()
-        outz = s.run_zero_copy()
+        outz = s.run_zero_copy().clone()
         torch.cuda.synchronize()
         assert torch.equal(outz.view(torch.uint8), out.view(torch.uint8)), name
+        wl = parts[name]
+        want = oracle_heads(f64(x[name]["q"]), f64(x[name]["k"]), f64(x[name]["v"]), 1.0 / math.sqrt(wl.D), wl.T,
+                            None)
+        got = f64(raw(outz))
+        assert np.isfinite(got).all()
+        err = np.max(np.abs(got - want))
+        assert err <= TOL, (name, err)
 
 
 def test_joint_av_concurrent_streams_match_sequential():
