@@ -710,39 +710,12 @@ def main():
                 "max_abs_diff_vs_step": float((step2.out.float() - step.out.float()).abs().max().item())}
         del step2
 
-    # -- relayout bandwidth with rotating buffer sets (> 1 GB in flight defeats the 256 MB MALL)
-    set_bytes = relayout_bytes
-    nsets = max(2, int(math.ceil(1.2e9 / max(set_bytes, 1))))
-    nsets = min(nsets, 16)
-    dt = step.kh.dtype
-    tok_shape = (B, Tp, H, D)
-    head_shape = (W, B, Tp, Hl, D)
-    sets = [([torch.empty(tok_shape, dtype=dt, device=dev) for _ in range(n_relayed)],
-             [torch.empty(head_shape, dtype=dt, device=dev) for _ in range(n_relayed)]) for _ in range(nsets)]
-    for s_, _ in sets:
-        for t in s_:
-            t.view(torch.uint8).random_()
-    tok_view = (Tp // W * H * D, Tp * H * D)
-    rl_iters = max(args.steps, 2 * nsets)
-    for i in range(nsets):
-        binding.sp_relayout_heads(sets[i][0], sets[i][1], W, B, Tp, H, D, binding.SP_TOKENS_TO_HEADS,
-                                  tok_strides=tok_view)
-    torch.cuda.synchronize()
-    r0 = torch.cuda.Event(enable_timing=True)
-    r1 = torch.cuda.Event(enable_timing=True)
-    r0.record(stream)
-    for i in range(rl_iters):
-        s_, d_ = sets[i % nsets]
-        binding.sp_relayout_heads(s_, d_, W, B, Tp, H, D, binding.SP_TOKENS_TO_HEADS, tok_strides=tok_view)
-    r1.record(stream)
-    torch.cuda.synchronize()
-    ms_relayout_rot = r0.elapsed_time(r1) / rl_iters
-    del sets
-    torch.cuda.empty_cache()
-
-    # -- the two gather kernels the same way, back to back over rotating
-    #    buffer sets (the in-step figures above include the gap between
-    #    launches, which weighs more on these 100 MB launches)
+    # -- the copy kernels back to back over rotating buffer sets (> 1 GB in
+    #    flight defeats the 256 MB MALL).  Each is timed twice: as eager
+    #    launches (the host's per-call work, Python and the binding included,
+    #    is longer than a 100 MB copy, so the GPU waits between launches) and
+    #    as one replay of the same launches recorded in a HIP graph (the
+    #    kernels back to back on the device); GB/s is the graph figure.
     def rotating_ms(make_set, call, nbytes):
         n = min(16, max(2, int(math.ceil(1.2e9 / max(nbytes, 1)))))
         bufs = [make_set() for _ in range(n)]
@@ -757,35 +730,55 @@ def main():
             call(*bufs[i % n])
         t1.record(stream)
         torch.cuda.synchronize()
-        del bufs
+        eager = t0.elapsed_time(t1) / iters
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            for i in range(iters):
+                call(*bufs[i % n])
+        g.replay()
+        torch.cuda.synchronize()
+        t0.record(stream)
+        g.replay()
+        t1.record(stream)
+        torch.cuda.synchronize()
+        graph = t0.elapsed_time(t1) / iters
+        del g, bufs
         torch.cuda.empty_cache()
-        return t0.elapsed_time(t1) / iters, n
+        return graph, eager, n
 
     def rand_like(t):
         u = torch.empty_like(t)
         u.view(torch.uint8).random_()
         return u
 
+    dt = step.kh.dtype
+    tok_view = (Tp // W * H * D, Tp * H * D)
+    ms_relayout_rot, ms_relayout_eager, nsets = rotating_ms(
+        lambda: ([rand_like(step.kh.new_empty((B, Tp, H, D))) for _ in range(n_relayed)],
+                 [torch.empty((W, B, Tp, Hl, D), dtype=dt, device=dev) for _ in range(n_relayed)]),
+        lambda srcs, dsts: binding.sp_relayout_heads(srcs, dsts, W, B, Tp, H, D, binding.SP_TOKENS_TO_HEADS,
+                                                     tok_strides=tok_view),
+        relayout_bytes)
     tq_pad = wl.q_tokens_pad if wl.cross else Tp
     t_out = wl.Tq if wl.cross else T
     ts_q = tq_pad // W
     # the two fused moves of the step, the same way
     unpadded = (B, T, H, D)
     fused_send_bytes = n_relayed * B * (T + Tp) * H * D * eb
-    ms_ps_rot, n_ps = rotating_ms(
+    ms_ps_rot, ms_ps_eager, n_ps = rotating_ms(
         lambda: ([rand_like(step.k.new_empty(unpadded)) for _ in range(n_relayed)],
                  [torch.empty_like(step.kh) for _ in range(n_relayed)]),
         lambda srcs, dsts: binding.sp_pad_relayout_heads(srcs, dsts, W, B, T, Tp, H, D),
         fused_send_bytes)
-    ms_ghu_rot, n_ghu = rotating_ms(
+    ms_ghu_rot, ms_ghu_eager, n_ghu = rotating_ms(
         lambda: (rand_like(step.oh), torch.empty_like(step.out)),
         lambda src, dst: binding.sp_gather_heads_unpad([src], [dst], W, B, tq_pad, H, D, t_out, counts=[ts_q] * W),
         gather_bytes)
-    ms_gh_rot, n_gh = rotating_ms(
+    ms_gh_rot, ms_gh_eager, n_gh = rotating_ms(
         lambda: (rand_like(step.oh), torch.empty_like(step.ot)),
         lambda src, dst: binding.sp_relayout_heads([src], [dst], W, B, tq_pad, H, D, binding.SP_HEADS_TO_TOKENS),
         relayout_o_bytes)
-    ms_gather_rot, n_ga = rotating_ms(
+    ms_gather_rot, ms_gather_eager, n_ga = rotating_ms(
         lambda: (rand_like(step.ot), torch.empty_like(step.out)),
         lambda src, dst: binding.sp_gather_unpad(src, dst, W, B, ts_q, H * D, t_out, counts=[ts_q] * W),
         gather_bytes)
@@ -855,6 +848,8 @@ def main():
                       "split": share_split}
     gbs = lambda nbytes, ms: nbytes / (ms * 1e-3) / 1e9
     kernels = {
+        "rotating_note": "copy kernels over rotating buffer sets: ms and GB/s from one replay of the launches "
+                         "recorded in a HIP graph; eager_ms with the launches issued one by one from Python",
         "pad+send_recv_heads": {"ms": round(ms_pad_send, 4), "bytes": run_bytes_in,
                                 "GB/s": round(gbs(run_bytes_in, ms_pad_send), 1),
                                 "note": "in the step: one fused move (plus the mask extension and the query pad "
@@ -865,10 +860,11 @@ def main():
         "pad+send_recv_heads_fused_rotating": {"ms": round(ms_ps_rot, 4), "bytes": fused_send_bytes,
                                                "GB/s": round(gbs(fused_send_bytes, ms_ps_rot), 1),
                                                "hbm_frac": round(gbs(fused_send_bytes, ms_ps_rot) / PEAK_HBM_GBS, 4),
-                                               "buffer_sets": n_ps},
+                                               "buffer_sets": n_ps, "eager_ms": round(ms_ps_eager, 4)},
         "gather_heads+gather_output_tokens_fused_rotating": {
             "ms": round(ms_ghu_rot, 4), "bytes": gather_bytes, "GB/s": round(gbs(gather_bytes, ms_ghu_rot), 1),
-            "hbm_frac": round(gbs(gather_bytes, ms_ghu_rot) / PEAK_HBM_GBS, 4), "buffer_sets": n_ghu},
+            "hbm_frac": round(gbs(gather_bytes, ms_ghu_rot) / PEAK_HBM_GBS, 4), "buffer_sets": n_ghu,
+            "eager_ms": round(ms_ghu_eager, 4)},
         "separate_moves_step": {"ms": round(ms_separate_step, 4),
                                 "pad+send_recv_heads_ms": round(ms_pad_send_sep, 4),
                                 "bytes_pad+send": pad_bytes + relayout_bytes,
@@ -876,7 +872,7 @@ def main():
         "send_recv_heads_rotating": {"ms": round(ms_relayout_rot, 4), "bytes": relayout_bytes,
                                      "GB/s": round(gbs(relayout_bytes, ms_relayout_rot), 1),
                                      "hbm_frac": round(gbs(relayout_bytes, ms_relayout_rot) / PEAK_HBM_GBS, 4),
-                                     "buffer_sets": nsets},
+                                     "buffer_sets": nsets, "eager_ms": round(ms_relayout_eager, 4)},
         "masked_attention": {"ms": round(ms_attn, 4), "back_to_back_ms": round(ms_attn_b2b, 4),
                              "back_to_back_TFLOP/s": round(attn_flops / (ms_attn_b2b * 1e-3) / 1e12, 2),
                              "TFLOP/s": round(attn_tflops, 2),
@@ -888,11 +884,11 @@ def main():
         "gather_heads_rotating": {"ms": round(ms_gh_rot, 4), "bytes": relayout_o_bytes,
                                   "GB/s": round(gbs(relayout_o_bytes, ms_gh_rot), 1),
                                   "hbm_frac": round(gbs(relayout_o_bytes, ms_gh_rot) / PEAK_HBM_GBS, 4),
-                                  "buffer_sets": n_gh},
+                                  "buffer_sets": n_gh, "eager_ms": round(ms_gh_eager, 4)},
         "gather_output_tokens_rotating": {"ms": round(ms_gather_rot, 4), "bytes": gather_bytes,
                                           "GB/s": round(gbs(gather_bytes, ms_gather_rot), 1),
                                           "hbm_frac": round(gbs(gather_bytes, ms_gather_rot) / PEAK_HBM_GBS, 4),
-                                          "buffer_sets": n_ga},
+                                          "buffer_sets": n_ga, "eager_ms": round(ms_gather_eager, 4)},
         "cp2d_step": cp2d,
         "zero_copy_step": {"ms": round(ms_zero, 4), "TFLOP/s": round(attn_flops / (ms_zero * 1e-3) / 1e12, 2),
                            "output_bytes_equal_to_step": zero_equal},

@@ -156,36 +156,49 @@ struct GatherHeadsUnpadArgs {
   uint32_t V;
   FastDiv fdV, fdRow;                 // by V and by W*V
   uint32_t chunks;                    // workgroups per rank (for the longest kept piece)
+  int32_t n_tensors;
   int64_t cum[kMaxWorldFused + 1];    // output row of each rank's first kept row
   uint32_t n_vec[kMaxWorldFused];     // kept rows * W*V of each rank (after the unpad)
 };
 
+// blockIdx.x = chunk, blockIdx.y = rank s, blockIdx.z = batch b; the
+// workgroup moves the same vectors of each tensor in turn.  The rank and
+// batch come straight from the grid, so the per-rank table loads do not wait
+// on a division (each workgroup moves 16 KiB per tensor, so the latency of
+// its first loads weighs).
 __global__ __launch_bounds__(kThreads) void gather_heads_unpad_kernel(GatherHeadsUnpadArgs a) {
-  const uint32_t s = blockIdx.x / a.chunks;
-  const uint32_t chunk = blockIdx.x - s * a.chunks;
-  const int64_t b = blockIdx.y;
-  const int n = blockIdx.z;
+  const uint32_t chunk = blockIdx.x;
+  const uint32_t s = blockIdx.y;
+  const int64_t b = blockIdx.z;
   const uint32_t nv = a.n_vec[s];
   const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
   if (chunk * uint32_t(kChunk) >= nv) return;
-  const char* src = a.src[n] + b * a.head_batch_b + int64_t(s) * a.seg_b;
-  char* dst = a.dst[n] + b * a.out_batch_b + a.cum[s] * a.row_b;
-  vec16 buf[kUnroll];
+  const int64_t src_off = b * a.head_batch_b + int64_t(s) * a.seg_b;
+  const int64_t dst_off = b * a.out_batch_b + a.cum[s] * a.row_b;
+  int64_t raddr[kUnroll];
 #pragma unroll
   for (int u = 0; u < kUnroll; ++u) {
     const uint32_t f = f0 + u * kThreads;
-    if (f < nv) {
-      const uint32_t t = fdiv(f, a.fdRow);
-      const uint32_t rem = f - t * a.fdRow.d;
-      const uint32_t r = fdiv(rem, a.fdV);
-      const uint32_t v = rem - r * a.V;
-      buf[u] = load16(src + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16);
-    }
+    const uint32_t t = fdiv(f, a.fdRow);
+    const uint32_t rem = f - t * a.fdRow.d;
+    const uint32_t r = fdiv(rem, a.fdV);
+    const uint32_t v = rem - r * a.V;
+    raddr[u] = src_off + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16;
   }
+  for (int n = 0; n < a.n_tensors; ++n) {
+    const char* src = a.src[n];
+    char* dst = a.dst[n] + dst_off;
+    vec16 buf[kUnroll];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < nv) store16(dst + int64_t(f) * 16, buf[u]);
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t f = f0 + u * kThreads;
+      if (f < nv) buf[u] = load16(src + raddr[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      const uint32_t f = f0 + u * kThreads;
+      if (f < nv) store16(dst + int64_t(f) * 16, buf[u]);
+    }
   }
 }
 
@@ -770,10 +783,9 @@ extern "C" sp_status sp_gather_heads_unpad(const void* const* src, void* const* 
   a.fdV = make_fastdiv(uint32_t(V));
   a.fdRow = make_fastdiv(uint32_t(V * W));
   a.chunks = uint32_t(div_up(max_vec, kChunk));
+  a.n_tensors = n_tensors;
   if (a.chunks == 0) return SP_OK;
-  const int64_t gx = int64_t(a.chunks) * W;
-  if (gx >= (int64_t(1) << 31)) return SP_ERR_UNSUPPORTED;
-  hipLaunchKernelGGL(gather_heads_unpad_kernel, dim3(unsigned(gx), unsigned(B), unsigned(n_tensors)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(gather_heads_unpad_kernel, dim3(a.chunks, unsigned(W), unsigned(B)), dim3(kThreads), 0,
                      as_stream(stream), a);
   return launch_status();
 }

@@ -242,49 +242,36 @@ class UlyssesStep:
             self.run()
         return g
 
-    # -- the same step with both exchanges folded into attention's addressing --
-    # On one device rank r's head-side view is a strided view of the padded
-    # token-side tensor: heads r*Hl.. of every token (rank stride Hl*D, token
-    # stride H*D).  Attention reads Q/K/V and writes O through those strides,
-    # so send_recv_heads and gather_heads move no bytes; the output lands in
-    # token layout, which gather_output_tokens then trims and unpads.  Same
-    # arithmetic in the same order as run(), hence the same bytes.
-    def attention_tokens(self):
+    # -- the same step with every move folded into attention's addressing -----
+    # On one device rank r's head-side view is a strided view of the token
+    # layout: heads r*Hl.. of every token (rank stride Hl*D, token stride
+    # H*D).  Attention reads Q/K/V and writes O through those strides, so
+    # send_recv_heads and gather_heads move no bytes.  Padding exists only so
+    # that the exchange splits the sequence evenly, so with no exchange the
+    # launch runs on the caller's unpadded tensors and mask (Tq = Tk = T, the
+    # user mask as given) and writes the final (B, T, H, D) output: pad, the
+    # mask extension and gather_output_tokens move no bytes either.  The real
+    # query rows see the same key tiles, visibility bits and summation order
+    # as in run() (the padded keys had zero weight; the padded rows are
+    # dropped by the unpad), hence the same bytes.
+    def attention_zero_copy(self):
         wl = self.wl
-        B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
-        if not hasattr(self, "oz"):
-            Tq = wl.q_tokens_pad if wl.cross else Tp
-            self.oz = torch.empty(B, Tq, H, D, dtype=self.kp.dtype, device=self.kp.device)
-            self.outz = torch.empty_like(self.out)
-        tok = (Hl * D, Tp * H * D, H * D, D)                 # rank, batch, token, head
-        if wl.cross:
-            Tq = wl.q_tokens_pad
-            qo = (Hl * D, Tq * H * D, H * D, D)
-            sp.sp_masked_attention(self.qc, self.kp, self.vp, self.oz, wl.W, B, Tq, Tp, Hl, D, qo, tok, tok, qo,
-                                   kv_valid_len=wl.T, scale=self.scale, workspace=self.workspace)
-        elif self.mask is not None:
-            sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
-                                   kv_valid_len=Tp, mask=self.mask_ext, scale=self.scale, workspace=self.workspace)
-        else:
-            sp.sp_masked_attention(self.qp, self.kp, self.vp, self.oz, wl.W, B, Tp, Tp, Hl, D, tok, tok, tok, tok,
-                                   kv_valid_len=wl.T, scale=self.scale, workspace=self.workspace)
-
-    def gather_output_tokens_z(self, lengths):
-        wl = self.wl
-        C = wl.H * wl.D
-        if wl.cross:
-            Tqp = wl.q_tokens_pad
-            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Tsq, C, wl.Tq, counts=[self.Tsq] * wl.W,
-                               in_strides=(self.Tsq * C, Tqp * C))
-        else:
-            sp.sp_gather_unpad(self.oz, self.outz, wl.W, wl.B, self.Ts, C, wl.T, counts=lengths,
-                               in_strides=(self.Ts * C, wl.T_pad * C))
+        B, T, Hl, D, H, W = wl.B, wl.T, wl.Hl, wl.D, wl.H, wl.W
+        Tq = wl.Tq if wl.cross else T
+        if not hasattr(self, "outz"):
+            self.outz = torch.empty(B, Tq, H, D, dtype=self.k.dtype, device=self.k.device)
+            mbs = 0 if self.mask is None or self.mask.shape[0] == 1 else T * T
+            need = sp.sp_masked_attention_workspace_size(W, B, Tq, T, Hl, D, sp._dtype_code(self.k),
+                                                         self.mask is not None, mbs)
+            self.workspace_z = torch.empty(need, dtype=torch.uint8, device=self.k.device) if need else None
+        qs = (Hl * D, Tq * H * D, H * D, D)                  # rank, batch, token, head
+        ks = (Hl * D, T * H * D, H * D, D)
+        sp.sp_masked_attention(self.q, self.k, self.v, self.outz, W, B, Tq, T, Hl, D, qs, ks, ks, qs,
+                               kv_valid_len=T, mask=self.mask, scale=self.scale, workspace=self.workspace_z)
 
     def run_zero_copy(self):
-        self.pad()
-        _, lengths = self.partition()
-        self.attention_tokens()
-        self.gather_output_tokens_z(lengths)
+        self.partition()
+        self.attention_zero_copy()
         return self.outz
 
 
