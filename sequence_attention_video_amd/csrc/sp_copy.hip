@@ -29,6 +29,39 @@ __device__ __forceinline__ void store16(char* p, vec16 v) {
   __builtin_nontemporal_store(v, reinterpret_cast<vec16*>(p));
 }
 
+// One thread's kUnroll vectors f0 + u*kThreads (u < kUnroll) of a range of n.
+// at(f, so, dof) sets vector f's source and destination byte offsets and
+// returns whether it is read (false: written as a zero vector).  With `full`
+// (uniform over the workgroup) the caller has checked that all of the
+// workgroup's vectors are below n and read: the loads then carry no
+// per-vector test and issue back to back, where guarded ones each wait for
+// the load before them (measured +4 to +7 % on 100 MB to 1 GB moves).
+template <typename Idx, typename At>
+__device__ __forceinline__ void move_vectors(const char* src, char* dst, Idx f0, Idx n, bool full, At at) {
+  vec16 buf[kUnroll];
+  int64_t so[kUnroll], dof[kUnroll];
+  if (full) {
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) {
+      at(f0 + Idx(u) * kThreads, so[u], dof[u]);
+      buf[u] = load16(src + so[u]);
+    }
+#pragma unroll
+    for (int u = 0; u < kUnroll; ++u) store16(dst + dof[u], buf[u]);
+    return;
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    const Idx f = f0 + Idx(u) * kThreads;
+    buf[u] = vec16{0, 0, 0, 0};
+    if (f < n && at(f, so[u], dof[u])) buf[u] = load16(src + so[u]);
+  }
+#pragma unroll
+  for (int u = 0; u < kUnroll; ++u) {
+    if (f0 + Idx(u) * kThreads < n) store16(dst + dof[u], buf[u]);
+  }
+}
+
 // ------------------------------------------------------------------ relayout
 
 struct RelayoutArgs {
@@ -65,29 +98,18 @@ __global__ __launch_bounds__(kThreads) void relayout_kernel(RelayoutArgs a) {
   char* dst = a.dst[n];
   const int64_t tok_off = s * a.tok_rank_b + b * a.tok_batch_b + r * a.run_b;
   const int64_t head_off = r * a.head_rank_b + b * a.head_batch_b + int64_t(s) * a.seg_b;
-
-  vec16 buf[kUnroll];
-  int64_t waddr[kUnroll];
-  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_seg) {
-      const uint32_t t = fdiv(f, a.fdV);
-      const uint32_t v = f - t * a.V;
-      const int64_t tok = tok_off + int64_t(t) * a.tok_row_b + int64_t(v) * 16;
-      const int64_t head = head_off + int64_t(f) * 16;
-      const int64_t raddr = a.to_heads ? tok : head;
-      waddr[u] = a.to_heads ? head : tok;
-      buf[u] = vec16{0, 0, 0, 0};
-      if (!a.to_heads || int64_t(s) * a.Ts + t < a.valid) buf[u] = load16(src + raddr);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_seg) store16(dst + waddr[u], buf[u]);
-  }
+  const uint32_t end = (chunk + 1) * uint32_t(kChunk);
+  const bool full = end <= a.n_per_seg && (!a.to_heads || int64_t(s) * a.Ts + fdiv(end - 1, a.fdV) < a.valid);
+  move_vectors(src, dst, chunk * uint32_t(kChunk) + threadIdx.x, a.n_per_seg, full,
+               [&](uint32_t f, int64_t& so, int64_t& dof) {
+                 const uint32_t t = fdiv(f, a.fdV);
+                 const uint32_t v = f - t * a.V;
+                 const int64_t tok = tok_off + int64_t(t) * a.tok_row_b + int64_t(v) * 16;
+                 const int64_t head = head_off + int64_t(f) * 16;
+                 so = a.to_heads ? tok : head;
+                 dof = a.to_heads ? head : tok;
+                 return !a.to_heads || int64_t(s) * a.Ts + t < a.valid;
+               });
 }
 
 // gather_heads walks the token side instead: every workgroup writes whole
@@ -120,24 +142,17 @@ __global__ __launch_bounds__(kThreads) void gather_heads_kernel(GatherHeadsArgs 
   const int n = blockIdx.z;
   const char* src = a.src[n] + b * a.head_batch_b + int64_t(s) * a.seg_b;
   char* dst = a.dst[n] + int64_t(s) * a.tok_rank_b + b * a.tok_batch_b;
-  vec16 buf[kUnroll];
-  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_shard) {
-      const uint32_t t = fdiv(f, a.fdRow);
-      const uint32_t rem = f - t * a.fdRow.d;
-      const uint32_t r = fdiv(rem, a.fdV);
-      const uint32_t v = rem - r * a.V;
-      buf[u] = load16(src + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_shard) store16(dst + int64_t(f) * 16, buf[u]);
-  }
+  const bool full = (chunk + 1) * uint32_t(kChunk) <= a.n_per_shard;
+  move_vectors(src, dst, chunk * uint32_t(kChunk) + threadIdx.x, a.n_per_shard, full,
+               [&](uint32_t f, int64_t& so, int64_t& dof) {
+                 const uint32_t t = fdiv(f, a.fdRow);
+                 const uint32_t rem = f - t * a.fdRow.d;
+                 const uint32_t r = fdiv(rem, a.fdV);
+                 const uint32_t v = rem - r * a.V;
+                 so = int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16;
+                 dof = int64_t(f) * 16;
+                 return true;
+               });
 }
 
 // gather_heads followed by gather_output_tokens as one move: rank s's token
@@ -166,18 +181,20 @@ struct GatherHeadsUnpadArgs {
 // batch come straight from the grid, so the per-rank table loads do not wait
 // on a division (each workgroup moves 16 KiB per tensor, so the latency of
 // its first loads weighs).
+template <int U>
 __global__ __launch_bounds__(kThreads) void gather_heads_unpad_kernel(GatherHeadsUnpadArgs a) {
+  constexpr uint32_t kVec = uint32_t(kThreads) * U;   // vectors per workgroup and tensor
   const uint32_t chunk = blockIdx.x;
   const uint32_t s = blockIdx.y;
   const int64_t b = blockIdx.z;
   const uint32_t nv = a.n_vec[s];
-  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
-  if (chunk * uint32_t(kChunk) >= nv) return;
+  const uint32_t f0 = chunk * kVec + threadIdx.x;
+  if (chunk * kVec >= nv) return;
   const int64_t src_off = b * a.head_batch_b + int64_t(s) * a.seg_b;
   const int64_t dst_off = b * a.out_batch_b + a.cum[s] * a.row_b;
-  int64_t raddr[kUnroll];
+  int64_t raddr[U];
 #pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
+  for (int u = 0; u < U; ++u) {
     const uint32_t f = f0 + u * kThreads;
     const uint32_t t = fdiv(f, a.fdRow);
     const uint32_t rem = f - t * a.fdRow.d;
@@ -185,19 +202,30 @@ __global__ __launch_bounds__(kThreads) void gather_heads_unpad_kernel(GatherHead
     const uint32_t v = rem - r * a.V;
     raddr[u] = src_off + int64_t(r) * a.head_rank_b + int64_t(t) * a.run_b + int64_t(v) * 16;
   }
+  // A workgroup whose vectors are all in range (all but the last of each
+  // rank) moves them with no per-vector test, so its loads issue back to
+  // back; guarded, each load would wait for the one before it.
+  const bool full = (chunk + 1) * kVec <= nv;
   for (int n = 0; n < a.n_tensors; ++n) {
     const char* src = a.src[n];
     char* dst = a.dst[n] + dst_off;
-    vec16 buf[kUnroll];
+    vec16 buf[U];
+    if (full) {
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t f = f0 + u * kThreads;
-      if (f < nv) buf[u] = load16(src + raddr[u]);
-    }
+      for (int u = 0; u < U; ++u) buf[u] = load16(src + raddr[u]);
 #pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      const uint32_t f = f0 + u * kThreads;
-      if (f < nv) store16(dst + int64_t(f) * 16, buf[u]);
+      for (int u = 0; u < U; ++u) store16(dst + int64_t(f0 + u * kThreads) * 16, buf[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t f = f0 + u * kThreads;
+        if (f < nv) buf[u] = load16(src + raddr[u]);
+      }
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const uint32_t f = f0 + u * kThreads;
+        if (f < nv) store16(dst + int64_t(f) * 16, buf[u]);
+      }
     }
   }
 }
@@ -230,28 +258,19 @@ __global__ __launch_bounds__(kThreads) void tile_2d_kernel(Tile2dArgs a) {
   const int64_t i = r / a.split_w, j = r - (r / a.split_w) * a.split_w;
   const int64_t tile_off = r * a.tile_rank_b + b * a.tile_batch_b;
   const int64_t grid_off = b * a.grid_batch_b + (i * a.th * a.width + j * a.tw) * a.row_b;
-  vec16 buf[kUnroll];
-  int64_t waddr[kUnroll];
-  const uint32_t f0 = blockIdx.x * uint32_t(kChunk) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_rb) {
-      const uint32_t run = fdiv(f, a.fd_runV);
-      const uint32_t v = f - run * a.runV;
-      const uint32_t fr = fdiv(run, a.fd_th);
-      const uint32_t y = run - fr * uint32_t(a.th);
-      const int64_t g = grid_off + ((int64_t(fr) * a.height + y) * a.width) * a.row_b + int64_t(v) * 16;
-      const int64_t t = tile_off + int64_t(f) * 16;
-      waddr[u] = a.to_tiles ? t : g;
-      buf[u] = load16(a.src + (a.to_tiles ? g : t));
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per_rb) store16(a.dst + waddr[u], buf[u]);
-  }
+  const bool full = (blockIdx.x + 1) * uint32_t(kChunk) <= a.n_per_rb;
+  move_vectors(a.src, a.dst, blockIdx.x * uint32_t(kChunk) + threadIdx.x, a.n_per_rb, full,
+               [&](uint32_t f, int64_t& so, int64_t& dof) {
+                 const uint32_t run = fdiv(f, a.fd_runV);
+                 const uint32_t v = f - run * a.runV;
+                 const uint32_t fr = fdiv(run, a.fd_th);
+                 const uint32_t y = run - fr * uint32_t(a.th);
+                 const int64_t g = grid_off + ((int64_t(fr) * a.height + y) * a.width) * a.row_b + int64_t(v) * 16;
+                 const int64_t t = tile_off + int64_t(f) * 16;
+                 so = a.to_tiles ? g : t;
+                 dof = a.to_tiles ? t : g;
+                 return true;
+               });
 }
 
 // ------------------------------------------------------------------ 2-D split + head exchange
@@ -292,27 +311,20 @@ __global__ __launch_bounds__(kThreads) void tile_2d_to_heads_kernel(Tile2dHeadsA
   const char* src = a.src[n] + b * a.grid_batch_b + r * a.run_b;
   char* dst = a.dst[n] + r * a.head_rank_b + b * a.head_batch_b + int64_t(s) * a.Tt * a.run_b;
   const int64_t row0 = i * a.th * a.width + j * a.tw;   // grid token of the tile's first token
-  vec16 buf[kUnroll];
-  const uint32_t f0 = chunk * uint32_t(kChunk) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per) {
-      const uint32_t t = fdiv(f, a.fdV);
-      const uint32_t v = f - t * a.V;
-      const uint32_t q = fdiv(t, a.fd_tw);
-      const uint32_t x = t - q * uint32_t(a.tw);
-      const uint32_t fr = fdiv(q, a.fd_th);
-      const uint32_t y = q - fr * uint32_t(a.th);
-      const int64_t g = row0 + (int64_t(fr) * a.height + y) * a.width + x;
-      buf[u] = load16(src + g * a.grid_row_b + int64_t(v) * 16);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per) store16(dst + int64_t(f) * 16, buf[u]);
-  }
+  const bool full = (chunk + 1) * uint32_t(kChunk) <= a.n_per;
+  move_vectors(src, dst, chunk * uint32_t(kChunk) + threadIdx.x, a.n_per, full,
+               [&](uint32_t f, int64_t& so, int64_t& dof) {
+                 const uint32_t t = fdiv(f, a.fdV);
+                 const uint32_t v = f - t * a.V;
+                 const uint32_t q = fdiv(t, a.fd_tw);
+                 const uint32_t x = t - q * uint32_t(a.tw);
+                 const uint32_t fr = fdiv(q, a.fd_th);
+                 const uint32_t y = q - fr * uint32_t(a.th);
+                 const int64_t g = row0 + (int64_t(fr) * a.height + y) * a.width + x;
+                 so = g * a.grid_row_b + int64_t(v) * 16;
+                 dof = int64_t(f) * 16;
+                 return true;
+               });
 }
 
 // blockIdx.x = chunk, blockIdx.y = batch b, blockIdx.z = tensor.  Flat
@@ -324,32 +336,25 @@ __global__ __launch_bounds__(kThreads) void tile_2d_from_heads_kernel(Tile2dHead
   const int n = blockIdx.z;
   const char* src = a.src[n] + b * a.head_batch_b;
   char* dst = a.dst[n] + b * a.grid_batch_b;
-  vec16 buf[kUnroll];
-  const uint32_t f0 = blockIdx.x * uint32_t(kChunk) + threadIdx.x;
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per) {
-      const uint32_t g = fdiv(f, a.fd_row);
-      const uint32_t rem = f - g * a.fd_row.d;
-      const uint32_t r = fdiv(rem, a.fdV);
-      const uint32_t v = rem - r * a.V;
-      const uint32_t q = fdiv(g, a.fd_width);
-      const uint32_t x_ = g - q * uint32_t(a.width);
-      const uint32_t fr = fdiv(q, a.fd_height);
-      const uint32_t y_ = q - fr * uint32_t(a.height);
-      const uint32_t i = fdiv(y_, a.fd_th), j = fdiv(x_, a.fd_tw);
-      const uint32_t y = y_ - i * uint32_t(a.th), x = x_ - j * uint32_t(a.tw);
-      const int64_t s = int64_t(i) * a.split_w + j;
-      const int64_t t = (int64_t(fr) * a.th + y) * a.tw + x;
-      buf[u] = load16(src + int64_t(r) * a.head_rank_b + (s * a.Tt + t) * a.run_b + int64_t(v) * 16);
-    }
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const uint32_t f = f0 + u * kThreads;
-    if (f < a.n_per) store16(dst + int64_t(f) * 16, buf[u]);
-  }
+  const bool full = (blockIdx.x + 1) * uint32_t(kChunk) <= a.n_per;
+  move_vectors(src, dst, blockIdx.x * uint32_t(kChunk) + threadIdx.x, a.n_per, full,
+               [&](uint32_t f, int64_t& so, int64_t& dof) {
+                 const uint32_t g = fdiv(f, a.fd_row);
+                 const uint32_t rem = f - g * a.fd_row.d;
+                 const uint32_t r = fdiv(rem, a.fdV);
+                 const uint32_t v = rem - r * a.V;
+                 const uint32_t q = fdiv(g, a.fd_width);
+                 const uint32_t x_ = g - q * uint32_t(a.width);
+                 const uint32_t fr = fdiv(q, a.fd_height);
+                 const uint32_t y_ = q - fr * uint32_t(a.height);
+                 const uint32_t i = fdiv(y_, a.fd_th), j = fdiv(x_, a.fd_tw);
+                 const uint32_t y = y_ - i * uint32_t(a.th), x = x_ - j * uint32_t(a.tw);
+                 const int64_t s = int64_t(i) * a.split_w + j;
+                 const int64_t t = (int64_t(fr) * a.th + y) * a.tw + x;
+                 so = int64_t(r) * a.head_rank_b + (s * a.Tt + t) * a.run_b + int64_t(v) * 16;
+                 dof = int64_t(f) * 16;
+                 return true;
+               });
 }
 
 // ------------------------------------------------------------------ pad
@@ -368,19 +373,13 @@ __global__ __launch_bounds__(kThreads) void pad_tokens_kernel(PadArgs a) {
   const int64_t b = blockIdx.y;
   const char* x = a.x + b * a.x_batch_b;
   char* y = a.y + b * a.y_batch_b;
-  const int64_t f0 = a.start_vec + int64_t(blockIdx.x) * kChunk + threadIdx.x;
-  vec16 buf[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t f = f0 + u * kThreads;
-    buf[u] = vec16{0, 0, 0, 0};
-    if (f < a.copy_vecs) buf[u] = load16(x + f * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t f = f0 + u * kThreads;
-    if (f < a.end_vec) store16(y + f * 16, buf[u]);
-  }
+  const int64_t first = a.start_vec + int64_t(blockIdx.x) * kChunk;
+  const bool full = first + kChunk <= a.copy_vecs;
+  move_vectors(x, y, first + threadIdx.x, a.end_vec, full, [&](int64_t f, int64_t& so, int64_t& dof) {
+    so = f * 16;
+    dof = f * 16;
+    return f < a.copy_vecs;
+  });
 }
 
 struct MaskPadArgs {
@@ -476,18 +475,13 @@ __global__ __launch_bounds__(kThreads) void gather_unpad_kernel(GatherArgs a) {
   const int64_t nvec = kept * a.row_b / 16;
   const char* src = a.in + r * a.rank_b + b * a.batch_b;
   char* dst = a.out + (b * a.T + first) * a.row_b;
-  const int64_t f0 = int64_t(blockIdx.x) * kChunk + threadIdx.x;
-  vec16 buf[kUnroll];
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t f = f0 + u * kThreads;
-    if (f < nvec) buf[u] = load16(src + f * 16);
-  }
-#pragma unroll
-  for (int u = 0; u < kUnroll; ++u) {
-    const int64_t f = f0 + u * kThreads;
-    if (f < nvec) store16(dst + f * 16, buf[u]);
-  }
+  const int64_t f_first = int64_t(blockIdx.x) * kChunk;
+  move_vectors(src, dst, f_first + threadIdx.x, nvec, f_first + kChunk <= nvec,
+               [&](int64_t f, int64_t& so, int64_t& dof) {
+                 so = f * 16;
+                 dof = f * 16;
+                 return true;
+               });
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -785,7 +779,7 @@ extern "C" sp_status sp_gather_heads_unpad(const void* const* src, void* const* 
   a.chunks = uint32_t(div_up(max_vec, kChunk));
   a.n_tensors = n_tensors;
   if (a.chunks == 0) return SP_OK;
-  hipLaunchKernelGGL(gather_heads_unpad_kernel, dim3(a.chunks, unsigned(W), unsigned(B)), dim3(kThreads), 0,
+  hipLaunchKernelGGL(gather_heads_unpad_kernel<kUnroll>, dim3(a.chunks, unsigned(W), unsigned(B)), dim3(kThreads), 0,
                      as_stream(stream), a);
   return launch_status();
 }
