@@ -298,8 +298,8 @@ void attn_bf16_kernel(AttnArgs a) {
   // partial, and each of those ends in a partial record (unnormalised O rows,
   // running max and sum) that attn_combine_kernel merges into O.
   const uint32_t gl = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0u;
-  int64_t u_next = SPLIT && !BAL ? int64_t(gl) * a.upw : 0;
-  int64_t u_end = SPLIT && !BAL ? (a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
+  int64_t u_next = SPLIT && !BAL ? uniform(int64_t(gl) * a.upw) : 0;
+  int64_t u_end = SPLIT && !BAL ? uniform(a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
   // Balanced split (masked launches whose items all share one mask): the
   // units are the non-empty key tiles of every item, so each workgroup's
   // range holds the same number of tiles that do work, where counting empty
@@ -354,15 +354,22 @@ void attn_bf16_kernel(AttnArgs a) {
     if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
   } else if constexpr (SPLIT) {
     if (u_next >= u_end) break;
-    item = uint32_t(u_next / a.nku);
-    kt_first = int(u_next - int64_t(item) * a.nku);
-    kt_stop = int(a.nku - kt_first < u_end - u_next ? a.nku : kt_first + (u_end - u_next));
-    u_next += kt_stop - kt_first;
+    item = uint32_t(uniform(int32_t(u_next / a.nku)));
+    kt_first = uniform(int32_t(u_next - int64_t(item) * a.nku));
+    kt_stop = uniform(int32_t(a.nku - kt_first < u_end - u_next ? a.nku : kt_first + (u_end - u_next)));
+    u_next = uniform(u_next + (kt_stop - kt_first));
     if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
   } else {
     item = MASK ? blockIdx.x : xcd_remap(blockIdx.x, a.nwg);
   }
-  const TileCoord tc = decode_item<MASK>(a, item);
+  // (the decode divides by runtime values in vector instructions; its results
+  // are uniform and kept in scalar registers, which leaves the vector
+  // registers to the tile loop)
+  TileCoord tc = decode_item<MASK>(a, item);
+  tc.r = uniform(tc.r);
+  tc.b = uniform(tc.b);
+  tc.head = uniform(tc.head);
+  tc.qt = uniform(tc.qt);
 
   const uint16_t* qp = static_cast<const uint16_t*>(a.q) + tc.r * a.qs[0] + tc.b * a.qs[1] + tc.head * a.qs[3];
   const uint16_t* kp = static_cast<const uint16_t*>(a.k) + tc.r * a.ks[0] + tc.b * a.ks[1] + tc.head * a.ks[3];
@@ -1290,17 +1297,18 @@ int64_t device_cus() {
 // measured on MI355X: ~4-5 us per tile-time at D = 128, ~15 us of fixed
 // cost).  With a user mask the units differ in cost (empty tiles are free),
 // so ranges stay shorter than an item (at most two segments), where the split
-// still bounds the critical path.  Returns upw when the split pays by 1.3x,
-// else 0: the model overprices a plain launch's last, partly filled round
-// (its CUs then run faster), e.g. the long_hires share, 688 query tiles,
-// measured 1.7 % slower split at a predicted 1.11x.
+// still bounds the critical path.  Returns upw when the split pays by 1.1x,
+// else 0.  The model overprices a plain launch's last, partly filled round
+// (its CUs then run faster): the long_hires share, 688 query tiles at 256
+// key tiles each, predicted 1.11x, measured 2 % faster split (3.83 against
+// 3.91 ms).
 int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D, bool masked) {
   if (items <= 0 || nku < 2 || ncu <= 0) return 0;
   const int64_t upw = div_up(items * nku, ncu);
   if (masked && upw >= nku) return 0;
   const int64_t plain = div_up(items, ncu) * nku;
   const int64_t fixed = 4 * 128 / D;
-  return plain * 10 >= (upw + fixed) * 13 ? upw : 0;
+  return plain * 10 >= (upw + fixed) * 11 ? upw : 0;
 }
 
 // query rows per workgroup of the bf16 kernel for head dim D (64 or 128)

@@ -282,10 +282,14 @@ def test_workspace_size(lib):
     # when no user mask makes the tiles' costs uneven
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == \
         2 * 256 * rec128
-    # the long_hires share, 688 query tiles of 256 key tiles, would gain less
-    # than the 1.3x the split asks for (three rounds unsplit, 688 + 4 tiles
-    # per CU split)
-    assert b.sp_masked_attention_workspace_size(1, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == 0
+    # the long_hires share, 688 query tiles of 256 key tiles: three rounds
+    # unsplit against 688 + 4 tile-times per CU split, 1.11x, above the 1.1x
+    # the split asks for
+    assert b.sp_masked_attention_workspace_size(1, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == \
+        2 * 256 * rec128
+    # and all eight shares of it, 5504 query tiles (22 rounds unsplit, 5508
+    # tile-times split: 1.02x), run unsplit
+    assert b.sp_masked_attention_workspace_size(8, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == 0
 
 
 def test_fast_division_host_twin(tmp_path):
