@@ -132,6 +132,14 @@ struct AttnArgs {
 
 // Query blocks a balanced split plans for (its per-block counts sit in LDS).
 constexpr int kMaxPlanBlocks = 512;
+// Units a balanced split charges for the start of an item's segment, on top
+// of its non-empty key tiles: a segment's Q load, first-tile wait and output
+// or record store take two to three tile-times at D = 128 (per-workgroup
+// timestamps on MI355X: ~6.5 us to the first tile and ~7 us of stores against
+// ~5.5 us per tile).  Without it the workgroups whose range meets two items
+// ran 1.35x the average time on the uneven-mask share; its split launch
+// measured 102.6 / 96.8 / 94.1 / 95.2 us at 0 / 2 / 3 / 4 units.
+constexpr int kSegmentCost = 3;
 
 // One partial record of a split launch: for BM query rows, O/l of the
 // segment rounded once to bf16 (rows of D), then m (running max, log2 units)
@@ -338,11 +346,15 @@ void attn_bf16_kernel(AttnArgs a) {
     }
     item = uint32_t(qi_cur * nrbh + p_cur);
     nnz_seg = uniform(a.plan_nnz[qi_cur]);
+    // an item's units: kSegmentCost units for its start, then its non-empty
+    // tiles; k_first, k_stop count them, and the segment runs tiles
+    // [k_first - kSegmentCost, k_stop - kSegmentCost) (clamped at 0)
+    const int32_t nu = nnz_seg + kSegmentCost;
     k_first = k_cur;
-    k_stop = int64_t(nnz_seg - k_first) < u_end - u_next ? nnz_seg : k_first + int32_t(u_end - u_next);
-    whole = k_first == 0 && k_stop == nnz_seg;
+    k_stop = int64_t(nu - k_first) < u_end - u_next ? nu : k_first + int32_t(u_end - u_next);
+    whole = k_first <= kSegmentCost && k_stop == nu;
     u_next += k_stop - k_first;
-    if (k_stop == nnz_seg) {
+    if (k_stop == nu) {
       k_cur = 0;
       if (++p_cur == nrbh) {
         p_cur = 0;
@@ -351,6 +363,10 @@ void attn_bf16_kernel(AttnArgs a) {
     } else {
       k_cur = k_stop;
     }
+    // (no range ends inside an item's start units: the plan ends it at the
+    // item's first unit instead, so every segment has tiles)
+    k_first = k_first > kSegmentCost ? k_first - kSegmentCost : 0;
+    k_stop -= kSegmentCost;
     if (seg > 0) __syncthreads();   // every wave is done with the previous segment's LDS tiles
   } else if constexpr (SPLIT) {
     if (u_next >= u_end) break;
@@ -846,15 +862,17 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
       for (int i = 0; i < DPT; i += 4) *reinterpret_cast<bf16x4*>(orow + d0 + i) = bf16x4{};
       return;
     }
-    u0 = a.plan_s[qi] + int64_t(int32_t(item) - qi * nrbh) * n;
-    u1 = u0 + n;
+    u0 = a.plan_s[qi] + int64_t(int32_t(item) - qi * nrbh) * (n + kSegmentCost);
+    u1 = u0 + n + kSegmentCost;
     upw = (a.plan_s[a.nqt] + a.split_wgs - 1) / a.split_wgs;
   } else {
     u0 = int64_t(item) * a.nku;
     u1 = u0 + a.nku;
     upw = a.upw;
   }
-  const int64_t g_first = u0 / upw, g_last = (u1 - 1) / upw;
+  // (with the balanced split, the workgroups that ran tiles of the item: a
+  // range that ends inside the item's start units ran none)
+  const int64_t g_first = (BAL ? u0 + kSegmentCost : u0) / upw, g_last = (u1 - 1) / upw;
   if (g_first == g_last) return;
   auto rec_of = [&](int64_t g) -> const char* {
     const int64_t slot = 2 * g + (g * upw < u0 ? 1 : 0);
@@ -1064,10 +1082,11 @@ __global__ __launch_bounds__(kThreads) void attn_f32_kernel(AttnArgs a) {
 
 // Plans a balanced split (see attn_bf16_kernel) from the class map of the
 // one mask every item shares: per query block (dispatch order, block qi =
-// query tile nqt-1-qi) the count of non-empty key tiles below kv_end, their
-// prefix sums over the items, and for each of the split_wgs logical
-// workgroups its range of units [u, u_end) with the block, the item of the
-// block and the non-empty tile of the item that unit u falls on.  One
+// query tile nqt-1-qi) the count of non-empty key tiles below kv_end, the
+// prefix sums of units over the items (an item's units: kSegmentCost, then
+// one per non-empty tile), and for each of the split_wgs logical workgroups
+// its range of units [u, u_end) with the block, the item of the block and the
+// unit of the item that unit u falls on.  One
 // workgroup; nqt <= kMaxPlanBlocks <= its threads.
 constexpr int kPlanThreads = 512;
 static_assert(kMaxPlanBlocks <= kPlanThreads, "one query block per thread in the prefix sum");
@@ -1089,7 +1108,10 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
     if (c != kTileEmpty) atomicAdd(&nnz[qi], 1);
   }
   __syncthreads();
-  if (tid < nqt) pre[tid] = int64_t(nnz[tid]) * nrbh;
+  // units of an item: its non-empty tiles plus kSegmentCost for its start
+  // (none for an item without a visible tile, which no workgroup runs)
+  auto units = [&](int qi) -> int64_t { return nnz[qi] ? nnz[qi] + kSegmentCost : 0; };
+  if (tid < nqt) pre[tid] = units(tid) * nrbh;
   __syncthreads();
   for (int off = 1; off < nqt; off *= 2) {
     const int64_t add = tid < nqt && tid >= off ? pre[tid - off] : 0;
@@ -1104,25 +1126,38 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
   }
   if (tid == 0) a.plan_s[nqt] = total;
   const int64_t upw = (total + a.split_wgs - 1) / a.split_wgs;
+  // the first block whose inclusive sum exceeds unit x (it has units, so x
+  // lies inside one of its items), and x's unit within its item
+  auto locate = [&](int64_t x, int& blk, int64_t& p, int64_t& k) {
+    int lo = 0, hi = nqt - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi) / 2;
+      if (pre[mid] > x) hi = mid; else lo = mid + 1;
+    }
+    const int64_t within = x - (lo == 0 ? 0 : pre[lo - 1]);
+    blk = lo;
+    p = within / units(lo);
+    k = within - p * units(lo);
+  };
   for (int g = tid; g < a.split_wgs; g += kPlanThreads) {
     const int64_t u = int64_t(g) * upw;
-    const int64_t u_end = total < u + upw ? total : u + upw;
+    int64_t u_end = total < u + upw ? total : u + upw;
     int64_t* st = a.plan_start + 4 * int64_t(g);
+    int blk;
+    int64_t p, k;
+    // a range whose last unit is one of an item's start units ends at the
+    // item's first unit instead (the next range runs the item)
+    if (u < u_end) {
+      locate(u_end - 1, blk, p, k);
+      if (k < kSegmentCost) u_end = u_end - 1 - k > u ? u_end - 1 - k : u;
+    }
     st[0] = u;
     st[1] = u_end;
     st[2] = 0;
     st[3] = 0;
     if (u >= u_end) continue;
-    // the first block whose inclusive sum exceeds u (it has units, so u lies
-    // inside one of its items)
-    int lo = 0, hi = nqt - 1;
-    while (lo < hi) {
-      const int mid = (lo + hi) / 2;
-      if (pre[mid] > u) hi = mid; else lo = mid + 1;
-    }
-    const int64_t within = u - (lo == 0 ? 0 : pre[lo - 1]);
-    const int64_t p = within / nnz[lo], k = within - p * nnz[lo];
-    st[2] = lo;
+    locate(u, blk, p, k);
+    st[2] = blk;
     st[3] = (p << 32) | k;
   }
 }

@@ -201,6 +201,32 @@ def test_attention_masked_split_uneven_work(D, Tq, Tk, Hl, blank):
         assert not got.any()
 
 
+@pytest.mark.parametrize("T,Hl,frame", [
+    (3000, 6, 400),     # 48 items of 1..24 visible key tiles, about 3 units per range
+    (1500, 16, 250),    # 64 items, ranges that start and end inside items' start units
+    (6150, 4, 384),     # the uneven-mask share's shape: frames of 384 tokens, 6 prompt tokens
+])
+def test_attention_balanced_split_block_causal(T, Hl, frame):
+    """Balanced split of a block-causal mask (frames see themselves and the
+    earlier frames, the trailing prompt tokens see and are seen by all): the
+    ranges count each item's non-empty key tiles plus the cost of a segment
+    start, so they begin and end inside items, inside items' start units (a
+    range that would end there stops at the item's first unit) and across
+    several whole items.  Every row against the oracle."""
+    say("attention balanced split block-causal", T, Hl, frame)
+    n_prompt = 6 if T % frame else 0
+    nv = T - n_prompt
+    idx = np.arange(T)
+    f = np.where(idx < nv, idx // frame, 1 << 20)
+    m = ((f[None, :] <= f[:, None]) | (idx[None, :] >= nv) | (idx[:, None] >= nv)).astype(np.uint8)[None]
+    need = sp.sp_masked_attention_workspace_size(1, 1, T, T, Hl, 128, sp.SP_BF16, True, 0)
+    plain = sp.sp_masked_attention_workspace_size(8, 1, T, T, 32 * Hl, 128, sp.SP_BF16, True, 0)
+    assert need > plain                      # the launch splits
+    got, want = run_case("bf16", 128, 1, 1, T, T, Hl, T, m, seed=T + Hl)
+    assert np.isfinite(got).all()
+    assert np.max(np.abs(got - want)) <= TOL["bf16"]
+
+
 @pytest.mark.parametrize("D,Tq,Tk,Hl,kv", [
     (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles, ranges of 38 tiles
     (64, 600, 4000, 100, 4000),     # 300 query tiles of 32 key tiles, ranges of 38 (two workgroups per CU)
