@@ -864,18 +864,25 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
     }
     u0 = a.plan_s[qi] + int64_t(int32_t(item) - qi * nrbh) * (n + kSegmentCost);
     u1 = u0 + n + kSegmentCost;
-    upw = (a.plan_s[a.nqt] + a.split_wgs - 1) / a.split_wgs;
+    upw = 0;
   } else {
     u0 = int64_t(item) * a.nku;
     u1 = u0 + a.nku;
     upw = a.upw;
   }
+  // the workgroup whose range holds unit x, and the first unit of range g
+  // (the balanced split's ranges: q = total / W units each, one more for the
+  // first rem = total % W)
+  const int64_t total = BAL ? a.plan_s[a.nqt] : 0, W = a.split_wgs;
+  const int64_t q = BAL ? total / W : upw, rem = BAL ? total - q * W : 0;
+  auto wg_of = [&](int64_t x) -> int64_t { return x < rem * (q + 1) ? x / (q + 1) : rem + (x - rem * (q + 1)) / q; };
+  auto start_of = [&](int64_t g) -> int64_t { return g * q + (g < rem ? g : rem); };
   // (with the balanced split, the workgroups that ran tiles of the item: a
   // range that ends inside the item's start units ran none)
-  const int64_t g_first = (BAL ? u0 + kSegmentCost : u0) / upw, g_last = (u1 - 1) / upw;
+  const int64_t g_first = wg_of(BAL ? u0 + kSegmentCost : u0), g_last = wg_of(u1 - 1);
   if (g_first == g_last) return;
   auto rec_of = [&](int64_t g) -> const char* {
-    const int64_t slot = 2 * g + (g * upw < u0 ? 1 : 0);
+    const int64_t slot = 2 * g + (start_of(g) < u0 ? 1 : 0);
     return a.part + slot * RL::kBytes;
   };
   float mx = -INFINITY;
@@ -1125,7 +1132,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
     a.plan_s[i] = i == 0 ? 0 : pre[i - 1];
   }
   if (tid == 0) a.plan_s[nqt] = total;
-  const int64_t upw = (total + a.split_wgs - 1) / a.split_wgs;
+  // workgroup g's range: q = total / W units, one more for the first
+  // total % W workgroups (W = split_wgs): every workgroup has work when there
+  // are W units or more, and any empty ranges come after all units
   // the first block whose inclusive sum exceeds unit x (it has units, so x
   // lies inside one of its items), and x's unit within its item
   auto locate = [&](int64_t x, int& blk, int64_t& p, int64_t& k) {
@@ -1140,8 +1149,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
     k = within - p * units(lo);
   };
   for (int g = tid; g < a.split_wgs; g += kPlanThreads) {
-    const int64_t u = int64_t(g) * upw;
-    int64_t u_end = total < u + upw ? total : u + upw;
+    const int64_t q = total / a.split_wgs, rem = total - q * a.split_wgs;
+    const int64_t u = g * q + (g < rem ? g : rem);
+    int64_t u_end = (g + 1) * q + (g + 1 < rem ? g + 1 : rem);
     int64_t* st = a.plan_start + 4 * int64_t(g);
     int blk;
     int64_t p, k;
