@@ -137,8 +137,9 @@ constexpr int kMaxPlanBlocks = 512;
 // or record store take two to three tile-times at D = 128 (per-workgroup
 // timestamps on MI355X: ~6.5 us to the first tile and ~7 us of stores against
 // ~5.5 us per tile).  Without it the workgroups whose range meets two items
-// ran 1.35x the average time on the uneven-mask share; its split launch
-// measured 102.6 / 96.8 / 94.1 / 95.2 us at 0 / 2 / 3 / 4 units.
+// set the critical path (1.21x the average workgroup time on a block-causal
+// share); the uneven-mask share's split launch measured 102.6 / 96.8 / 94.1
+// / 95.2 us at 0 / 2 / 3 / 4 units.
 constexpr int kSegmentCost = 3;
 
 // One partial record of a split launch: for BM query rows, O/l of the
@@ -309,17 +310,17 @@ void attn_bf16_kernel(AttnArgs a) {
   int64_t u_next = SPLIT && !BAL ? uniform(int64_t(gl) * a.upw) : 0;
   int64_t u_end = SPLIT && !BAL ? uniform(a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
   // Balanced split (masked launches whose items all share one mask): the
-  // units are the non-empty key tiles of every item, so each workgroup's
-  // range holds the same number of tiles that do work, where counting empty
-  // tiles too (above) leaves the ranges over long query tiles with several
-  // times the work of the others.  Items come query block by query block
-  // (block qi is query tile nqt-1-qi), (rank, batch, head) fastest, so every
-  // item of a block has the block's count of non-empty tiles
-  // (a.plan_nnz).  plan_balanced_split_kernel has written where this
-  // workgroup's range starts: block qi_cur, item p_cur of the block,
-  // non-empty tile k_cur of the item.  (Planned in a kernel of its own: the
-  // same planning inside this kernel pushed Q fragments out to scratch in
-  // the tile loop.)
+  // units are the non-empty key tiles of every item, after kSegmentCost
+  // units for the item's start, so each workgroup's range holds the same
+  // work, where counting empty tiles too (above) leaves the ranges over long
+  // query tiles with several times the work of the others.  Items come query
+  // block by query block (block qi is query tile nqt-1-qi), (rank, batch,
+  // head) fastest, so every item of a block has the block's count of
+  // non-empty tiles (a.plan_nnz).  plan_balanced_split_kernel has written
+  // where this workgroup's range starts: block qi_cur, item p_cur of the
+  // block, unit k_cur of the item.  (Planned in a kernel of its own: the same
+  // planning inside this kernel pushed Q fragments out to scratch in the tile
+  // loop.)
   int32_t qi_cur = 0, p_cur = 0, k_cur = 0;
   const int32_t nrbh = int32_t(a.nwg / uint32_t(a.nqt));          // items per query block
   const int32_t nku_b = int32_t((a.kv_end + KT - 1) / KT);          // key tiles below kv_end
@@ -1132,11 +1133,8 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
     a.plan_s[i] = i == 0 ? 0 : pre[i - 1];
   }
   if (tid == 0) a.plan_s[nqt] = total;
-  // workgroup g's range: q = total / W units, one more for the first
-  // total % W workgroups (W = split_wgs): every workgroup has work when there
-  // are W units or more, and any empty ranges come after all units
   // the first block whose inclusive sum exceeds unit x (it has units, so x
-  // lies inside one of its items), and x's unit within its item
+  // lies inside one of its items), the item of the block and x's unit in it
   auto locate = [&](int64_t x, int& blk, int64_t& p, int64_t& k) {
     int lo = 0, hi = nqt - 1;
     while (lo < hi) {
@@ -1148,6 +1146,9 @@ __global__ __launch_bounds__(kPlanThreads) void plan_balanced_split_kernel(AttnA
     p = within / units(lo);
     k = within - p * units(lo);
   };
+  // workgroup g's range: q = total / W units, one more for the first
+  // total % W workgroups (W = split_wgs): every workgroup has work when there
+  // are W units or more, and any empty ranges come after all units
   for (int g = tid; g < a.split_wgs; g += kPlanThreads) {
     const int64_t q = total / a.split_wgs, rem = total - q * a.split_wgs;
     const int64_t u = g * q + (g < rem ? g : rem);
