@@ -197,9 +197,17 @@ def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
     share = main[2 + n:]
     groups = [("all W rank shares (one launch)", main[1:1 + n], flops_all),
               ("rank 0's share alone (R = 1)", share, flops_share)]
-    merge = [d for d in order if "combine" in kname[d] and d > main[1 + n]][1:]
+    # a split launch's merge kernel follows its attention kernel: each merge
+    # dispatch belongs to the attention dispatch before it
+    merge_of = {}
+    for d in order:
+        if "combine" in kname[d]:
+            prev = [m for m in main if m < d]
+            if prev:
+                merge_of[prev[-1]] = d
     rows, recs = [], []
     for label, ds, flops in groups:
+        merge = [merge_of[d] for d in ds if d in merge_of]
         avg = lambda f: sum(f(d) for d in ds) / len(ds)
         busy = avg(lambda d: per[d]["SQ_VALU_MFMA_BUSY_CYCLES"]) / N_SIMD
         hw = avg(lambda d: per[d]["SQ_INSTS_VALU_MFMA_MOPS_BF16"]) * 512
@@ -212,7 +220,7 @@ def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
                "mfma_busy_cycles_per_simd": int(busy), "mfma_util_at_peak_clock": round(util_peak, 4),
                "mfma_busy_of_active_cycles": round(util_active, 4), "active_cycles_per_xcd": int(gui),
                "implied_clock_ghz": round(gui / t / 1e9, 3)}
-        if label.startswith("rank") and merge:
+        if merge:
             rec["merge_kernel_us"] = round(sum(dur[d] for d in merge) / len(merge) * 1e6, 1)
         recs.append(rec)
         rows.append(f"| {label} | `{rec['kernel']}` | {rec['us_per_launch']} | {flops:.4g} | {hw:.4g} | "
@@ -237,9 +245,10 @@ def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
              "| launch | kernel | us per launch | algorithmic flops | hw MFMA flops | hw / alg | MFMA util at 2.4 GHz | "
              "MFMA busy of active cycles | implied clock (GHz) |",
              "|---|---|---|---|---|---|---|---|---|"] + rows
-    if any("merge_kernel_us" in r for r in recs):
-        lines += ["", f"The share's split launch is followed by a merge kernel (`attn_combine_kernel`) of "
-                      f"{recs[-1]['merge_kernel_us']} us per launch (no MFMA work)."]
+    for r in recs:
+        if "merge_kernel_us" in r:
+            lines += ["", f"The split launch of {r['launch']} is followed by a merge kernel (`attn_combine_kernel`) "
+                          f"of {r['merge_kernel_us']} us per launch (no MFMA work)."]
     lines += ["", "mfma_json: " + json.dumps(out)]
     path = os.path.join(ROOT, "profiles", f"attention_mfma_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
@@ -331,15 +340,23 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
         # the probe's first attention dispatch is the step's (all W shares);
         # the share launches have another grid
         g_all = next((grid[i] for i in ids if is_attn(i)), None)
-        all_ = [per[i] for i in ids if is_attn(i) and grid[i] == g_all]
-        share = [per[i] for i in ids if is_attn(i) and grid[i] != g_all]
-        comb = [per[i] for i in ids if "attn_combine_kernel" in kname[i]]
+        # a split launch's merge kernel follows its attention kernel and
+        # counts with it
+        merged = dict((i, per[i]) for i in ids if is_attn(i))
+        last = None
+        for i in ids:
+            if is_attn(i):
+                last = i
+            elif "attn_combine_kernel" in kname[i] and last is not None:
+                merged[last] += per[i]
+        all_ = [merged[i] for i in ids if is_attn(i) and grid[i] == g_all]
+        share = [merged[i] for i in ids if is_attn(i) and grid[i] != g_all]
         cls = [per[i] for i in ids if "classify_mask_kernel" in kname[i]]
         avg = lambda v: sum(v) / len(v) if v else float("nan")
         first = lambda key: next((per[i] for i in ids if key in kname[i]), float("nan"))
         out[name] = {"copy_kib": copy_kib, "scale": scale,
                      "all_kib": avg(all_[1:]) if len(all_) > 1 else avg(all_),
-                     "share_kib": avg(share[1:]) + (avg(comb[1:]) if len(comb) > 1 else 0.0),
+                     "share_kib": avg(share[1:]),
                      "classify_kib": avg(cls), "send_kib": first("relayout_kernel"),
                      "pad_mask_kib": first("pad_mask_kernel"), "gather_kib": first("gather_heads_unpad_kernel")}
     b = lambda ctr, key: out[ctr][key] * out[ctr]["scale"] * 1024
@@ -368,7 +385,7 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
         f_, w_ = b("FETCH_SIZE", key), b("WRITE_SIZE", key)
         ratio = (f_ + w_) / alg if alg else float("nan")
         lines.append(f"| {label} | {f_:.4g} | {w_:.4g} | {f_ + w_:.4g} | {alg:.4g} | {ratio:.3f} |")
-    row("attention, all W rank shares (R = W)", "all_kib", alg_all)
+    row("attention, all W rank shares (R = W; a split launch's merge included)", "all_kib", alg_all)
     row("attention, rank 0's share alone (R = 1; a split launch's merge included)", "share_kib", alg_all // wl.W)
     nrel = 2 if wl.cross else 3
     send_alg = nrel * (wl.B * wl.T * wl.H * wl.D * wl.eb + one)
@@ -402,7 +419,8 @@ def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd:
     bench = json.loads([l for l in open(bench_json).read().splitlines() if l.startswith('{"metric"')][-1])
     wl = WORKLOADS[bench["config"]["workload"]]
     groups = collections.defaultdict(list)
-    for r in csv.DictReader(open(trace_csv)):
+    rows = sorted(csv.DictReader(open(trace_csv)), key=lambda r: int(r["Start_Timestamp"]))
+    for r in rows:
         grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
         dur = (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
         groups[(r["Kernel_Name"], grid)].append(dur)
@@ -411,6 +429,16 @@ def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd:
     # the all-ranks launch is the attention grid launched most often; any
     # other attention grid is rank 0's share alone
     g_all = max(((g, len(v)) for (n, g), v in groups.items() if is_attn(n)), key=lambda t: t[1], default=(None, 0))[0]
+    # a split launch's merge kernel follows its attention kernel: a merge
+    # grid belongs to the attention launch dispatched before it
+    merge_kind, last = {}, None
+    for r in rows:
+        grid = int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"])
+        if is_attn(r["Kernel_Name"]):
+            last = grid
+        elif "attn_combine_kernel" in r["Kernel_Name"] and last is not None:
+            merge_kind[(r["Kernel_Name"], grid)] = ("merge of the all-ranks launch" if last == g_all
+                                                    else "merge of the split share")
     lines = [f"# {title}", "", "Command (run from the repository root on one MI355X):", "", "```", cmd, "```", "",
              "Dispatches grouped by kernel and grid size (threads).", "",
              "| kernel | grid | launch | calls | avg (us) | median (us) | min (us) | max (us) | share of time |",
@@ -421,12 +449,13 @@ def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd:
         short = name.replace("sp::(anonymous namespace)::", "")
         short = short if len(short) <= 80 else short[:77] + "..."
         kind = ("all ranks (R = %d)" % wl.W if grid == g_all else "one share (R = 1)") if is_attn(name) else (
-            "merge of the split share" if "attn_combine_kernel" in name else "")
+            merge_kind.get((name, grid), "merge") if "attn_combine_kernel" in name else "")
         lines.append(f"| `{short}` | {grid} | {kind} | {len(v)} | {sum(v) / len(v):.1f} | "
                      f"{statistics.median(v):.1f} | {min(v):.1f} | {max(v):.1f} | {100 * sum(v) / total:.1f}% |")
     r, rs, k = bench["roofline"], bench.get("roofline_share") or {}, bench["kernels"]
     lines += ["", "The same run's bench line (HIP events on the launch stream):", "",
-              f"* attention, all ranks: {r['avg_launch_ms'] * 1e3:.1f} us per launch (median in the step), "
+              f"* attention, all ranks{' (split + merge)' if r.get('split') else ''}: "
+              f"{r['avg_launch_ms'] * 1e3:.1f} us per launch (median in the step), "
               f"{r['achieved']} TFLOP/s, {100 * r['frac']:.1f}% of the bf16 MFMA peak"]
     if rs:
         lines.append(f"* attention, one share (R = 1{', split + merge' if rs.get('split') else ''}): "
@@ -796,6 +825,13 @@ def main():
     mask_part = binding.sp_masked_attention_workspace_size(1, B, tq_share, Tp, Hl, D, binding.SP_F32,
                                                            step.mask is not None, mbs)
     share_split = wl.dtype == "bf16" and need > mask_part
+    # the all-ranks launch splits too where its query tiles leave a partly
+    # filled last round (long_hires: 21 whole rounds of 256, then 128 tiles)
+    all_split = wl.dtype == "bf16" and (
+        binding.sp_masked_attention_workspace_size(W, B, tq_share, Tp, Hl, D, binding._dtype_code(step.kh),
+                                                   step.mask is not None, mbs) >
+        binding.sp_masked_attention_workspace_size(W, B, tq_share, Tp, Hl, D, binding.SP_F32,
+                                                   step.mask is not None, mbs))
     share_ws = torch.empty(need, dtype=torch.uint8, device=dev) if need else None
     n_share = 10 if attn_flops > 4e12 else max(20, args.steps)
     for _ in range(n_share):
@@ -836,8 +872,8 @@ def main():
     kname = ("attn_bf16_kernel<%d>" % D) if wl.dtype == "bf16" and D in (64, 128) else ("attn_f32_kernel<%d>" % D)
     roofline = {"bound": "mfma", "achieved": round(attn_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",
                 "frac": round(attn_tflops / peak_mfma, 4), "traffic": traffic,
-                "kernel": kname, "flops_per_launch": attn_flops,
-                "avg_launch_ms": round(ms_attn, 4), "R": W}
+                "kernel": kname + (" + attn_combine_kernel" if all_split else ""), "flops_per_launch": attn_flops,
+                "avg_launch_ms": round(ms_attn, 4), "R": W, "split": all_split}
     # one rank's share alone (R = 1): what each GPU runs when the ranks are
     # devices; a split launch is the attention kernel plus the merge kernel
     roofline_share = {"bound": "mfma", "achieved": round(share_tflops, 2), "peak": peak_mfma, "unit": "TFLOP/s",

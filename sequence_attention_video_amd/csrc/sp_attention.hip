@@ -117,10 +117,13 @@ struct AttnArgs {
   int32_t nqt_cls;                       // query tiles of the class map
   float c;                               // scale * log2(e)
   uint32_t nwg;
-  // split launches (bf16): the key tiles of all items in order
-  int64_t units;                         // items * nku (balanced split: unused, planned on the device)
-  int64_t upw;                           // units per workgroup (< nku)
+  // split launches (bf16): items [0, n_direct) run whole, one workgroup
+  // each, as in a plain launch; the key tiles of the others, item after
+  // item, are cut into ranges
+  int64_t units;                         // nwg * nku (balanced split: unused, planned on the device)
+  int64_t upw;                           // units per range
   int32_t nku;                           // key tiles of KT per item
+  uint32_t n_direct;                     // items run whole before the ranges (0 with a user mask)
   char* part;                            // partial records, two per workgroup (RecordLayout)
   // balanced split of a masked launch (see attn_bf16_kernel): workgroups of
   // the launch, and the plan written by logical workgroup 0 for the merge
@@ -301,14 +304,29 @@ void attn_bf16_kernel(AttnArgs a) {
   // Work split.  Without SPLIT a workgroup runs one item over all of its key
   // tiles.  With SPLIT (launches whose items do not divide evenly over the
   // GPU) the key tiles of all items, item after item, form one sequence of
-  // units, and logical workgroup g runs units [g*upw, (g+1)*upw): one segment
-  // per item it meets.  A segment that covers a whole item ends like an
-  // unsplit one; only the first and the last segment of a range can be
-  // partial, and each of those ends in a partial record (unnormalised O rows,
-  // running max and sum) that attn_combine_kernel merges into O.
-  const uint32_t gl = SPLIT ? xcd_remap(blockIdx.x, gridDim.x) : 0u;
-  int64_t u_next = SPLIT && !BAL ? uniform(int64_t(gl) * a.upw) : 0;
-  int64_t u_end = SPLIT && !BAL ? uniform(a.units < u_next + a.upw ? a.units : u_next + a.upw) : 0;
+  // units.  The first n_direct workgroups run items [0, n_direct) whole, one
+  // each (whole rounds of the GPU, dispatched first, as in a plain launch);
+  // after them logical range g (workgroup n_direct + g before the remap)
+  // runs units n_direct*nku + [g*upw, (g+1)*upw), one segment per item it
+  // meets.  A segment that covers a whole item ends like an unsplit one; only
+  // the first and the last segment of a range can be partial, and each of
+  // those ends in a partial record (O/l rows, running max and sum) that
+  // attn_combine_kernel merges into O.  So the dispatcher fills the last,
+  // partly filled round of a plain launch with ranges of equal work.
+  const bool run_whole = SPLIT && !MASK && blockIdx.x < a.n_direct;
+  const uint32_t gl = !SPLIT || run_whole ? 0u
+                      : BAL              ? xcd_remap(blockIdx.x, gridDim.x)
+                                         : xcd_remap(blockIdx.x - a.n_direct, gridDim.x - a.n_direct);
+  int64_t u_next = 0, u_end = 0;
+  if constexpr (SPLIT && !BAL) {
+    if (run_whole) {
+      u_next = uniform(int64_t(xcd_remap(blockIdx.x, a.n_direct)) * a.nku);
+      u_end = u_next + a.nku;
+    } else {
+      u_next = uniform(int64_t(a.n_direct) * a.nku + int64_t(gl) * a.upw);
+      u_end = uniform(a.units < u_next + a.upw ? a.units : u_next + a.upw);
+    }
+  }
   // Balanced split (masked launches whose items all share one mask): the
   // units are the non-empty key tiles of every item, after kSegmentCost
   // units for the item's start, so each workgroup's range holds the same
@@ -825,11 +843,11 @@ void attn_bf16_kernel(AttnArgs a) {
   }   // segments
 }
 
-// Merges the partial records of split launches: for every row of every item,
-// O = sum_s w_s (O/l)_s / sum_s w_s with w_s = 2^(m_s - M) l_s and M = max_s
-// m_s (the running rescale's algebra, applied once), 0 where no key was
-// visible.  One workgroup per (item, 32 rows); kMergeTpr threads per row,
-// each D / kMergeTpr dims.  The records' m values are read first, then each
+// Merges the partial records of split launches: for every row of every item
+// the ranges ran (items n_direct and on), O = sum_s w_s (O/l)_s / sum_s w_s
+// with w_s = 2^(m_s - M) l_s and M = max_s m_s (the running rescale's
+// algebra, applied once), 0 where no key was visible.  One workgroup per
+// (item, 32 rows); kMergeTpr threads per row, each D / kMergeTpr dims.  The records' m values are read first, then each
 // record's weight and O/l, their loads independent of the running sums.
 constexpr int kMergeTpr = 8;
 constexpr int kMergeRows = kThreads / kMergeTpr;   // rows per merge workgroup
@@ -840,7 +858,7 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
   constexpr int BM = kRows<D>;
   constexpr int DPT = D / kMergeTpr;   // dims per thread (16 or 8: two or one 16-byte loads)
   static_assert(DPT % 8 == 0, "whole 16-byte groups of bf16 per thread");
-  const uint32_t item = blockIdx.x;
+  const uint32_t item = (BAL ? 0u : a.n_direct) + blockIdx.x;
   const int row = blockIdx.y * kMergeRows + int(threadIdx.x) / kMergeTpr;
   const int d0 = (int(threadIdx.x) % kMergeTpr) * DPT;
   const TileCoord tc = decode_item<MASK>(a, item);
@@ -867,7 +885,8 @@ __global__ __launch_bounds__(kThreads) void attn_combine_kernel(AttnArgs a) {
     u1 = u0 + n + kSegmentCost;
     upw = 0;
   } else {
-    u0 = int64_t(item) * a.nku;
+    // (units counted from the first range's, n_direct * nku)
+    u0 = int64_t(item - a.n_direct) * a.nku;
     u1 = u0 + a.nku;
     upw = a.upw;
   }
@@ -1293,9 +1312,11 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
                              0, s, a);
         }
       } else if (a.part) {
-        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>), dim3(unsigned((a.units + a.upw - 1) / a.upw)),
+        hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, true>),
+                           dim3(a.n_direct + unsigned((a.units - int64_t(a.n_direct) * a.nku + a.upw - 1) / a.upw)),
                            dim3(64 * kWaves<D>), 0, s, a);
-        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg, kRows<D> / kMergeRows), dim3(kThreads), 0, s, a);
+        hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg - a.n_direct, kRows<D> / kMergeRows),
+                           dim3(kThreads), 0, s, a);
       } else {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(64 * kWaves<D>), 0, s, a);
       }
@@ -1335,26 +1356,39 @@ int64_t device_cus() {
   return n;
 }
 
-// Split decision for the bf16 kernel, per CU: with `items` query tiles of
-// nku key tiles each, a plain launch takes ceil(items / ncu) * nku
-// tile-times; a split launch takes upw = ceil(items * nku / ncu) plus a
-// fixed cost for the partial records and the merge launch, about 4
-// tile-times at D = 128 and twice that at D = 64 (a tile costs half as much;
-// measured on MI355X: ~4-5 us per tile-time at D = 128, ~15 us of fixed
-// cost).  With a user mask the units differ in cost (empty tiles are free),
-// so ranges stay shorter than an item (at most two segments), where the split
-// still bounds the critical path.  Returns upw when the split pays by 1.1x,
-// else 0.  The model overprices a plain launch's last, partly filled round
-// (its CUs then run faster): the long_hires share, 688 query tiles at 256
-// key tiles each, predicted 1.11x, measured 2 % faster split (3.83 against
-// 3.91 ms).
-int64_t split_units_per_wg(int64_t items, int64_t nku, int64_t ncu, int32_t D, bool masked) {
-  if (items <= 0 || nku < 2 || ncu <= 0) return 0;
-  const int64_t upw = div_up(items * nku, ncu);
-  if (masked && upw >= nku) return 0;
-  const int64_t plain = div_up(items, ncu) * nku;
+// Split decision for the bf16 kernel, per CU, with `items` query tiles of
+// nku key tiles each.  Without a user mask the whole rounds of a plain
+// launch, floor(items / ncu) * ncu items, run as they would there (dispatched
+// first, one workgroup per item), and only the rest, `tail` items, can be
+// split: a plain launch runs them in one more round of nku tile-times, a
+// split in ranges of upw = ceil(tail * nku / ncu) key tiles plus a fixed
+// cost for the partial records and the merge launch, about 4 tile-times at
+// D = 128 and twice that at D = 64 (a tile costs half as much; measured on
+// MI355X: ~4-5 us per tile-time at D = 128, ~15 us of fixed cost).  With a
+// user mask the units differ in cost (empty tiles are free): no items run
+// whole, and ranges stay shorter than an item (at most two segments), where
+// the split still bounds the critical path.  The split runs when it pays by
+// 1.1x: the model overprices a plain launch's partly filled round (its CUs
+// then run faster).
+struct SplitPlan {
+  int64_t upw = 0;        // key tiles per range; 0: no split
+  int64_t n_direct = 0;   // items run whole before the ranges
+};
+SplitPlan split_plan(int64_t items, int64_t nku, int64_t ncu, int32_t D, bool masked) {
+  SplitPlan p;
+  if (items <= 0 || nku < 2 || ncu <= 0) return p;
+  const int64_t nd = masked ? 0 : items / ncu * ncu;
+  const int64_t tail = items - nd;
+  if (tail == 0) return p;
+  const int64_t upw = div_up(tail * nku, ncu);
+  if (masked && upw >= nku) return p;
+  const int64_t plain = div_up(tail, ncu) * nku;
   const int64_t fixed = 4 * 128 / D;
-  return plain * 10 >= (upw + fixed) * 11 ? upw : 0;
+  if (plain * 10 >= (upw + fixed) * 11) {
+    p.upw = upw;
+    p.n_direct = nd;
+  }
+  return p;
 }
 
 // query rows per workgroup of the bf16 kernel for head dim D (64 or 128)
@@ -1413,7 +1447,7 @@ extern "C" size_t sp_masked_attention_workspace_size(int32_t R, int64_t B, int64
     const int64_t ncu = device_cus();
     const int64_t nqt = div_up(Tq, bf16_rows(D));
     const int64_t items = nqt * Hl * B * R;
-    if (split_units_per_wg(items, div_up(Tk, KT), ncu, D, has_mask != 0)) {
+    if (split_plan(items, div_up(Tk, KT), ncu, D, has_mask != 0).upw) {
       split = split_bytes(ncu, D);
       if (balanced_split(has_mask != 0, D, mask_batch_stride, B, nqt)) split += plan_bytes(nqt, ncu);
     }
@@ -1496,7 +1530,7 @@ sp_status attn_check(const void* q, sp_attn_strides qs, const void* k, sp_attn_s
   a.nqt = int32_t(nqt); a.nkt = int32_t(nkt); a.nqt_cls = int32_t(nqt_cls);
   a.c = c2;
   a.nwg = uint32_t(nwg);
-  a.units = 0; a.upw = 0; a.nku = 0; a.part = nullptr;
+  a.units = 0; a.upw = 0; a.nku = 0; a.n_direct = 0; a.part = nullptr;
   a.split_wgs = 0; a.plan_nnz = nullptr; a.plan_s = nullptr; a.plan_start = nullptr;
   c.dtype = dtype;
   c.D = D;
@@ -1524,7 +1558,8 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
   if (bf16_mfma_kernel(c.dtype, c.D)) {
     const int64_t ncu = device_cus();
     const int64_t nku = div_up(a.kv_end, KT);
-    const int64_t upw = split_units_per_wg(c.nwg, nku, ncu, c.D, c.has_mask);
+    const SplitPlan sp = split_plan(c.nwg, nku, ncu, c.D, c.has_mask);
+    const int64_t upw = sp.upw;
     // the split runs only with room for its partial records after the mask
     // part (as sized by sp_masked_attention_workspace_size); otherwise the
     // plain launch runs
@@ -1533,6 +1568,7 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
     const int64_t part_at = plan_at + (bal ? plan_bytes(a.nqt, ncu) : 0);
     if (upw && workspace && workspace_bytes >= size_t(part_at + split_bytes(ncu, c.D)) &&
         (reinterpret_cast<uintptr_t>(workspace) & 255) == 0) {
+      a.n_direct = uint32_t(sp.n_direct);
       a.units = c.nwg * nku; a.upw = upw; a.nku = int32_t(nku);
       a.part = static_cast<char*>(workspace) + part_at;
       if (bal) {

@@ -277,19 +277,23 @@ def test_workspace_size(lib):
     assert b.sp_masked_attention_workspace_size(8, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == 0
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 1024, 4, 64, b.SP_BF16, False, 0) == 0
     assert b.sp_masked_attention_workspace_size(1, 1, 6144, 6144, 4, 64, b.SP_F32, False, 0) == 0
-    # 544 query tiles of 49 key tiles take three rounds of 256 CUs unsplit and
-    # 105 tiles per CU split, so eight shares of the 6152-token workload split
-    # when no user mask makes the tiles' costs uneven
+    # Past whole rounds of the GPU only the rest of the query tiles can split.
+    # 544 query tiles of 49 key tiles: two whole rounds, then 32 tiles that
+    # take one more round of 49 tile-times unsplit against ranges of 7 (+ 4
+    # for the records and the merge) split, so eight shares of the
+    # 6152-token workload split when no user mask makes the tiles' costs uneven
     assert b.sp_masked_attention_workspace_size(8, 1, 6152, 6152, 4, 128, b.SP_BF16, False, 0) == \
         2 * 256 * rec128
-    # the long_hires share, 688 query tiles of 256 key tiles: three rounds
-    # unsplit against 688 + 4 tile-times per CU split, 1.11x, above the 1.1x
-    # the split asks for
+    # the long_hires share, 688 query tiles of 256 key tiles: two whole
+    # rounds, then 176 tiles: 256 tile-times unsplit against 176 + 4 split
     assert b.sp_masked_attention_workspace_size(1, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == \
         2 * 256 * rec128
-    # and all eight shares of it, 5504 query tiles (22 rounds unsplit, 5508
-    # tile-times split: 1.02x), run unsplit
-    assert b.sp_masked_attention_workspace_size(8, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == 0
+    # all eight shares of it, 5504 query tiles: 21 whole rounds, then 128
+    # tiles: 256 tile-times unsplit against 128 + 4 split
+    assert b.sp_masked_attention_workspace_size(8, 2, 32768, 32768, 4, 128, b.SP_BF16, False, 0) == \
+        2 * 256 * rec128
+    # a whole number of rounds never splits: 1024 query tiles
+    assert b.sp_masked_attention_workspace_size(16, 1, 6144, 6144, 4, 128, b.SP_BF16, False, 0) == 0
 
 
 def test_fast_division_host_twin(tmp_path):

@@ -228,14 +228,16 @@ def test_attention_balanced_split_block_causal(T, Hl, frame):
 
 
 @pytest.mark.parametrize("D,Tq,Tk,Hl,kv", [
-    (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles, ranges of 38 tiles
-    (64, 600, 4000, 100, 4000),     # 300 query tiles of 32 key tiles, ranges of 38 (two workgroups per CU)
+    (128, 1000, 4000, 100, 3990),   # 300 query tiles of 32 key tiles: 256 run whole, 44 in ranges of 6 tiles
+    (64, 600, 4000, 100, 4000),     # the same counts at D = 64 (two workgroups per CU)
 ])
 def test_attention_split_ranges_spanning_items(D, Tq, Tk, Hl, kv):
-    """More query tiles than CUs, unevenly: the split's ranges cover whole
-    items (written directly) and pieces of others (merged from records).  The
-    oracle checks a sample of heads holding both kinds; every other row is
-    checked to be finite and written."""
+    """More query tiles than CUs, unevenly: one whole round of items runs as
+    in a plain launch, and the rest are cut into ranges that cover pieces of
+    items (merged from records), some crossing from one item into the next.
+    The oracle checks a sample of heads holding both kinds (head 85 holds
+    query tile 255, the last whole one, and tiles 256, 257, the first in
+    ranges); every other row is checked to be finite and written."""
     say("attention split spanning items", D, Tq, Tk, Hl, kv)
     ws = sp.sp_masked_attention_workspace_size(1, 1, Tq, Tk, Hl, D, sp.SP_BF16, False, 0)
     assert ws > 0
@@ -250,7 +252,7 @@ def test_attention_split_ranges_spanning_items(D, Tq, Tk, Hl, kv):
     torch.cuda.synchronize()
     got = raw(o)
     assert np.isfinite(f64(got)).all()
-    heads = [0, 1, 2, Hl // 2, Hl // 2 + 1, Hl - 2, Hl - 1]
+    heads = [0, 1, 2, Hl // 2, 85, 86, Hl - 2, Hl - 1]
     want = O.attention_heads(f64(q[0][:, :, heads]), f64(k[0][:, :, heads]), f64(v[0][:, :, heads]),
                              1 / math.sqrt(D), kv)
     err = np.max(np.abs(f64(got[0][:, :, heads]) - want))
