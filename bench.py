@@ -444,7 +444,7 @@ def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd:
              "| kernel | grid | launch | calls | avg (us) | median (us) | min (us) | max (us) | share of time |",
              "|---|---|---|---|---|---|---|---|---|"]
     for (name, grid), v in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
-        if sum(v) < 0.001 * total:
+        if sum(v) < 0.001 * total and "attn_combine_kernel" not in name:
             continue
         short = name.replace("sp::(anonymous namespace)::", "")
         short = short if len(short) <= 80 else short[:77] + "..."
