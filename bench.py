@@ -30,6 +30,7 @@ import sys
 import time
 
 ROOT = os.path.dirname(os.path.abspath(__file__))
+PROFILE_DIR = os.path.join(ROOT, "profiles")   # rocprofv3 summaries (read and written here)
 sys.path.insert(0, ROOT)
 
 METRIC = "masked-attention TFLOP/s (MFMA util %) + head relayout GB/s (HBM %), 1 GPU"
@@ -69,7 +70,7 @@ def read_traffic(workload: str, src_hash: str, key: str = "bytes_per_launch"):
     "share_bytes_per_launch" for one rank's share) from the committed
     rocprofv3 counter summary, if it was taken on the current kernel source;
     else None."""
-    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+    path = os.path.join(PROFILE_DIR, f"attention_traffic_{workload}.md")
     if not os.path.exists(path):
         return None
     text = open(path, encoding="utf-8").read()
@@ -250,7 +251,7 @@ def write_mfma_summary(workload: str, pmc_dir: str, cmds: list):
             lines += ["", f"The split launch of {r['launch']} is followed by a merge kernel (`attn_combine_kernel`) "
                           f"of {r['merge_kernel_us']} us per launch (no MFMA work)."]
     lines += ["", "mfma_json: " + json.dumps(out)]
-    path = os.path.join(ROOT, "profiles", f"attention_mfma_{workload}.md")
+    path = os.path.join(PROFILE_DIR, f"attention_mfma_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print(open(path).read())
@@ -296,7 +297,7 @@ def write_pipe_summary(workload: str, pmc_dir: str, cmds: list):
              f"All-ranks launch (`{rec['kernel']}`), averages over {len(ds)} launches (the probe's first, the step's, "
              "left out). SQ instruction counts are wave instructions summed over the GPU.", "",
              "| quantity | value |", "|---|---|"] + [f"| {q} | {v:.3f} |" for q, v in rows] +             ["", "pipe_json: " + json.dumps(rec)]
-    path = os.path.join(ROOT, "profiles", f"attention_pipes_{workload}.md")
+    path = os.path.join(PROFILE_DIR, f"attention_pipes_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print(open(path).read())
@@ -400,7 +401,7 @@ def write_traffic_summary(workload: str, fetch_dir: str, write_dir: str, cmds: l
         row("mask classifier (`classify_mask_kernel`: mask read, classes and words written)", "classify_kib",
             Tp * Tp + Tp * nkt * 8)
     lines += ["", "traffic_json: " + json.dumps(rec)]
-    path = os.path.join(ROOT, "profiles", f"attention_traffic_{workload}.md")
+    path = os.path.join(PROFILE_DIR, f"attention_traffic_{workload}.md")
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print(open(path).read())
@@ -471,7 +472,7 @@ def write_kernel_trace_summary(trace_csv: str, bench_json: str, title: str, cmd:
             lines.append(f"* {label}: {k[key]['ms'] * 1e3:.1f} us, {k[key]['GB/s']} GB/s "
                          f"({100 * k[key]['hbm_frac']:.1f}% of 8000 GB/s)")
     lines.append(f"* kernel source hash: `{bench['kernel_source_hash']}`")
-    path = os.path.join(ROOT, "profiles", out_name)
+    path = os.path.join(PROFILE_DIR, out_name)
     with open(path, "w", encoding="utf-8") as f:
         f.write("\n".join(lines) + "\n")
     print(open(path).read())
