@@ -847,8 +847,9 @@ void attn_bf16_kernel(AttnArgs a) {
 // the ranges ran (items n_direct and on), O = sum_s w_s (O/l)_s / sum_s w_s
 // with w_s = 2^(m_s - M) l_s and M = max_s m_s (the running rescale's
 // algebra, applied once), 0 where no key was visible.  One workgroup per
-// (item, 32 rows); kMergeTpr threads per row, each D / kMergeTpr dims.  The records' m values are read first, then each
-// record's weight and O/l, their loads independent of the running sums.
+// (item, 32 rows); kMergeTpr threads per row, each D / kMergeTpr dims.  The
+// records' m values are read first, then each record's weight and O/l, their
+// loads independent of the running sums.
 constexpr int kMergeTpr = 8;
 constexpr int kMergeRows = kThreads / kMergeTpr;   // rows per merge workgroup
 
