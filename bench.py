@@ -526,7 +526,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         msg = ("bench.py measures one GPU only: the W ranks of the sequence-parallel path are virtual "
-               "ranks on a single device in this build; multi-GPU runs are not supported")
+               "ranks on a single device; runs on several GPUs are not supported")
         if int(os.environ.get("RANK", "0")) == 0:
             print(msg, file=sys.stderr, flush=True)
         sys.exit(2)

@@ -1,5 +1,5 @@
-"""bench.py's output contract: one JSON line with the fields the driver and
-the roofline report read.  The multi-GPU refusal runs on the host; one short
+"""bench.py's output contract: one JSON line with the fields that benchmark
+harnesses and the roofline report read.  The multi-GPU refusal runs on the host; one short
 run of the tiny workload runs on the GPU."""
 
 import json
