@@ -72,6 +72,12 @@ template <int D>
 constexpr int kWaves = D == 64 ? 8 : 12;
 template <int D>
 constexpr int kWavesPerSimd = D == 64 ? 4 : 3;
+// D = 64 launches whose items would leave at least half of the GPU's
+// workgroup slots empty run 4-wave workgroups of 128 query rows instead (no
+// user mask, unsplit): twice the workgroups over the same work, two per CU
+// (cross_v2a's share, 96 query tiles of 256 rows: 25.4 -> 20.6 us; the
+// all-ranks launch, which fills the GPU, measured 11 % slower so).
+constexpr int kNarrowWaves64 = 4;
 // query rows per bf16 workgroup, and the height of the mask-class tiles of
 // bf16 launches
 template <int D>
@@ -237,7 +243,6 @@ template <int D>
 struct Bf16Tile {
   static constexpr int KPG = 512 / D;               // keys per 1 KiB group
   static constexpr int NG = KT / KPG;               // groups per tile = direct loads per tile
-  static constexpr int NLD = (NG + kWaves<D> - 1) / kWaves<D>;   // direct loads per wave per tile and tensor (at most)
   static constexpr int GROUP_BYTES = 1024 + 64;
   static constexpr int TILE_BYTES = NG * GROUP_BYTES;
   static constexpr int NKS = D / 16;                // k-steps of QK^T
@@ -261,13 +266,17 @@ __device__ __forceinline__ void wait_vmem() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | 0x70 | 0xF00);
 }
 
-template <int D, bool MASK, bool SPLIT, bool BAL = false>
-__global__ __launch_bounds__(64 * kWaves<D>) __attribute__((amdgpu_waves_per_eu(kWavesPerSimd<D>)))
+template <int D, bool MASK, bool SPLIT, bool BAL = false, int WAVES = kWaves<D>>
+__global__ __launch_bounds__(64 * WAVES)
+__attribute__((amdgpu_waves_per_eu(WAVES == kWaves<D> ? kWavesPerSimd<D> : kWavesPerSimd<D> * WAVES / kWaves<D>)))
 void attn_bf16_kernel(AttnArgs a) {
   static_assert(!BAL || (MASK && SPLIT), "the balanced split is a split of masked launches");
-  constexpr int WAVES = kWaves<D>, THREADS = 64 * WAVES, BM = kRows<D>;
+  // (class tiles and partial records are kRows<D> rows high)
+  static_assert(WAVES == kWaves<D> || (!MASK && !SPLIT), "narrow workgroups only for plain launches");
+  constexpr int THREADS = 64 * WAVES, BM = 32 * QB * WAVES;
   using T = Bf16Tile<D>;
-  constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NLD = T::NLD, NG = T::NG;
+  constexpr int NKS = T::NKS, NDB = T::NDB, KPG = T::KPG, NG = T::NG;
+  constexpr int NLD = (NG + WAVES - 1) / WAVES;   // direct loads per wave per tile and tensor (at most)
   constexpr int LOADS = 2 * NLD;   // direct loads per wave per tile (K and V)
   // Each buffer is its own LDS object, so that the compiler can tell which
   // buffer a direct load writes and never waits on it before reading another.
@@ -1301,7 +1310,7 @@ bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
 bool bf16_mfma_kernel(sp_dtype dt, int32_t D) { return dt == SP_BF16 && (D == 64 || D == 128); }
 
 template <int D, bool MASK>
-void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
+void launch_attn(const AttnArgs& a, sp_dtype dt, bool narrow, hipStream_t s) {
   if (bf16_mfma_kernel(dt, D)) {
     if constexpr (D % 32 == 0) {
       if (a.part && a.split_wgs > 0) {
@@ -1318,6 +1327,10 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
                            dim3(64 * kWaves<D>), 0, s, a);
         hipLaunchKernelGGL((attn_combine_kernel<D, MASK>), dim3(a.nwg - a.n_direct, kRows<D> / kMergeRows),
                            dim3(kThreads), 0, s, a);
+      } else if (narrow) {
+        if constexpr (D == 64 && !MASK)
+          hipLaunchKernelGGL((attn_bf16_kernel<D, false, false, false, kNarrowWaves64>), dim3(a.nwg),
+                             dim3(64 * kNarrowWaves64), 0, s, a);
       } else {
         hipLaunchKernelGGL((attn_bf16_kernel<D, MASK, false>), dim3(a.nwg), dim3(64 * kWaves<D>), 0, s, a);
       }
@@ -1330,11 +1343,11 @@ void launch_attn(const AttnArgs& a, sp_dtype dt, hipStream_t s) {
 }
 
 template <bool MASK>
-sp_status dispatch_d(int D, const AttnArgs& a, sp_dtype dt, hipStream_t s) {
+sp_status dispatch_d(int D, const AttnArgs& a, sp_dtype dt, bool narrow, hipStream_t s) {
   switch (D) {
-    case 16: launch_attn<16, MASK>(a, dt, s); break;
-    case 64: launch_attn<64, MASK>(a, dt, s); break;
-    case 128: launch_attn<128, MASK>(a, dt, s); break;
+    case 16: launch_attn<16, MASK>(a, dt, narrow, s); break;
+    case 64: launch_attn<64, MASK>(a, dt, narrow, s); break;
+    case 128: launch_attn<128, MASK>(a, dt, narrow, s); break;
     default: return SP_ERR_UNSUPPORTED;
   }
   return launch_status();
@@ -1556,6 +1569,7 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
   a.bits = c.has_mask ? reinterpret_cast<const uint64_t*>(static_cast<const char*>(workspace) +
                                                           cls_ws_bytes(c.bm, a.Tq, a.Tk, c.crows))
                       : nullptr;
+  bool narrow = false;
   if (bf16_mfma_kernel(c.dtype, c.D)) {
     const int64_t ncu = device_cus();
     const int64_t nku = div_up(a.kv_end, KT);
@@ -1581,6 +1595,14 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
         a.plan_start = reinterpret_cast<int64_t*>(plan + plan_starts_at(a.nqt));
       }
     }
+    // an unsplit D = 64 launch without a user mask whose items fill at most
+    // one of each CU's two workgroup slots: 4-wave workgroups of 128 rows
+    if (c.D == 64 && !c.has_mask && a.part == nullptr && c.nwg <= ncu) {
+      narrow = true;
+      const int64_t per_tile = c.nwg / a.nqt;   // items per query tile: R * B * Hl
+      a.nqt = int32_t(div_up(a.Tq, 32 * QB * kNarrowWaves64));
+      a.nwg = uint32_t(per_tile * a.nqt);
+    }
   }
   if (c.has_mask) {
     hipLaunchKernelGGL(classify_mask_kernel, dim3(unsigned(div_up(c.nkt, kClsSpan)), unsigned(c.nqt_cls), unsigned(c.bm)),
@@ -1588,9 +1610,9 @@ sp_status attn_run(AttnCall& c, void* workspace, size_t workspace_bytes, hipStre
                        s, a.mask, a.mask_bs, a.Tq, a.Tk, int32_t(c.nqt_cls), int32_t(c.nkt),
                        static_cast<uint8_t*>(workspace), const_cast<uint64_t*>(a.bits), a.ldw, int32_t(c.crows));
     if (launch_status() != SP_OK) return SP_ERR_HIP;
-    return dispatch_d<true>(c.D, a, c.dtype, s);
+    return dispatch_d<true>(c.D, a, c.dtype, narrow, s);
   }
-  return dispatch_d<false>(c.D, a, c.dtype, s);
+  return dispatch_d<false>(c.D, a, c.dtype, narrow, s);
 }
 
 }  // namespace
