@@ -1229,7 +1229,7 @@ __global__ __launch_bounds__(kClsThreads) void classify_mask_kernel(const uint8_
   static_assert(BN == 64, "one 64-bit word per row and class tile");
   constexpr int kWavesC = kClsThreads / 64;
   __shared__ uint64_t words[kClsSpan * kClsMaxRows];   // [class tile][row]
-  __shared__ int any_s[kClsSpan], all_s[kClsSpan];
+  __shared__ int any_w[kWavesC], all_w[kWavesC];         // per wave: some word non-zero, every word full
   const int span = blockIdx.x, qt = blockIdx.y;
   const int64_t b = blockIdx.z;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -1239,10 +1239,6 @@ __global__ __launch_bounds__(kClsThreads) void classify_mask_kernel(const uint8_
   const bool aligned8 = ((reinterpret_cast<uintptr_t>(mask) | uintptr_t(mask_bs) | uintptr_t(Tk)) & 7) == 0;
   const int64_t left = Tq - int64_t(qt) * rows;
   const int nrows = int(left < rows ? left : rows);
-  if (threadIdx.x < kClsSpan) {
-    any_s[threadIdx.x] = 0;
-    all_s[threadIdx.x] = 1;
-  }
   uint8_t* wbytes = reinterpret_cast<uint8_t*>(words);
   const uint8_t* base = mask + b * mask_bs + int64_t(qt) * rows * Tk + key;
   for (int r0 = w; r0 < nrows; r0 += kWavesC * kClsUnroll) {
@@ -1267,23 +1263,45 @@ __global__ __launch_bounds__(kClsThreads) void classify_mask_kernel(const uint8_
     }
   }
   __syncthreads();
-  // words out, rows contiguous per class tile; the classes by OR / AND (every
-  // writer of a flag writes the same value, so plain stores suffice)
-  for (int i = threadIdx.x; i < kClsSpan * nrows; i += kClsThreads) {
-    const int ci = i / nrows, r = i - ci * nrows;
+  // Words out, rows contiguous per class tile: waves kWavesPerTile*ci ..
+  // take class tile ci, each wave 64 consecutive rows per store (512
+  // contiguous bytes), and fold its words into the tile's class with two
+  // ballots (a per-thread row index divided by nrows, and a flag store from
+  // every lane, had made this phase longer than reading the mask).
+  constexpr int kWavesPerTile = kWavesC / kClsSpan;
+  static_assert(kWavesC % kClsSpan == 0, "whole waves per class tile");
+  {
+    const int ci = w / kWavesPerTile;
     const int cti = span * kClsSpan + ci;
-    if (cti >= nkt) continue;
-    const uint64_t word = words[ci * kClsMaxRows + r];
-    bits[(b * nkt + cti) * ldw + int64_t(qt) * rows + r] = word;
-    const int64_t n = Tk - int64_t(cti) * BN < BN ? Tk - int64_t(cti) * BN : BN;   // in-range keys
-    const uint64_t full = n >= 64 ? ~0ull : ((1ull << n) - 1);
-    if (word != 0) any_s[ci] = 1;
-    if (word != full) all_s[ci] = 0;
+    bool any = false, all = true;
+    if (cti < nkt) {
+      const int64_t n = Tk - int64_t(cti) * BN < BN ? Tk - int64_t(cti) * BN : BN;   // in-range keys
+      const uint64_t full = n >= 64 ? ~0ull : ((1ull << n) - 1);
+      uint64_t* dst = bits + (b * nkt + cti) * ldw + int64_t(qt) * rows;
+      for (int r = (w % kWavesPerTile) * 64 + lane; r < nrows; r += 64 * kWavesPerTile) {
+        const uint64_t word = words[ci * kClsMaxRows + r];
+        dst[r] = word;
+        any = any || word != 0;
+        all = all && word == full;
+      }
+    }
+    const bool wave_any = __ballot(any) != 0, wave_all = __ballot(!all) == 0;
+    if (lane == 0) {
+      any_w[w] = wave_any;
+      all_w[w] = wave_all;
+    }
   }
   __syncthreads();
-  if (threadIdx.x < kClsSpan && span * kClsSpan + int(threadIdx.x) < nkt)
+  if (threadIdx.x < kClsSpan && span * kClsSpan + int(threadIdx.x) < nkt) {
+    bool any = false, all = true;
+#pragma unroll
+    for (int j = 0; j < kWavesPerTile; ++j) {
+      any = any || any_w[threadIdx.x * kWavesPerTile + j];
+      all = all && all_w[threadIdx.x * kWavesPerTile + j];
+    }
     cls[(b * nqt + qt) * int64_t(nkt) + span * kClsSpan + threadIdx.x] =
-        !any_s[threadIdx.x] ? kTileEmpty : (all_s[threadIdx.x] ? kTileFull : kTilePartial);
+        !any ? kTileEmpty : (all ? kTileFull : kTilePartial);
+  }
 }
 
 int64_t div_up(int64_t a, int64_t b) { return (a + b - 1) / b; }
