@@ -194,14 +194,16 @@ sp_status sp_gather_heads_unpad(const void* const* src, void* const* dst, int32_
  * workspace: device scratch of sp_masked_attention_workspace_size() bytes,
  * 256-byte aligned, rewritten by every call; may be NULL when that size is 0.
  * With a mask it holds per-tile mask classes and bit-packed mask rows and is
- * required.  For bf16 it may also hold, after that part, the float32 partial
- * results of a split launch: when the query tiles do not spread evenly over
- * the GPU (one rank's share of a few heads, or a count a little above a
- * multiple of the compute units), the key tiles of all query tiles are cut
- * into one equal range per compute unit and a second kernel merges the
- * partial results.  Without room for them (NULL or a smaller workspace) the
- * same call runs unsplit: same result up to float32 summation order, slower
- * on such shapes.
+ * required.  For bf16 it may also hold, after that part, the partial results
+ * of a split launch (per query row, O/l rounded once to bf16 and the running
+ * max and sum in float32): when the query tiles do not spread evenly over the
+ * GPU (one rank's share of a few heads, or a count a little above a multiple
+ * of the compute units), the query tiles of whole rounds of the GPU run
+ * unsplit, the key tiles of the others are cut into one equal range per
+ * compute unit, and a second kernel merges the partial results.  Without room
+ * for them (NULL or a smaller workspace) the same call runs unsplit: the same
+ * result up to float32 summation order and that one extra rounding (at most
+ * 2^-9 of |O|), slower on such shapes.
  * Supported: D in {16, 64, 128} for both types.  SP_BF16 at D = 64 and 128
  * runs bf16 MFMA with float32 softmax and accumulation; SP_BF16 at D = 16
  * widens the bf16 values exactly to float32 and runs float32 MFMA; SP_F32
