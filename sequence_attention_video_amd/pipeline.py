@@ -147,9 +147,9 @@ class UlyssesStep:
     def attention_rank(self, r: int, out, workspace=None):
         """Rank r's share alone (R = 1): the attention launch one GPU runs when
         the ranks are real devices.  out: (B, Tq, Hl, D) head-side buffer.  A
-        share has few query tiles, so without a user mask the library splits
-        the key range over the GPU (workspace from the size query, allocated
-        here when not given)."""
+        share has few query tiles, so the library usually splits their key
+        ranges over the GPU (by non-empty tiles under a user mask; workspace
+        from the size query, allocated here when not given)."""
         wl = self.wl
         B, Tp, Hl, D, H = wl.B, wl.T_pad, wl.Hl, wl.D, wl.H
         head_side = (B * Tp * Hl * D, Tp * Hl * D, Hl * D, D)
