@@ -55,6 +55,8 @@ CASES = [
     ("bf16", 64, 1, 1, 1000, 1024, 4, 987, None),       # few query tiles: 4-wave workgroups of 128 rows, ragged
     ("bf16", 64, 1, 1, 2048, 300, 32, 300, None),       # 256 query tiles of 256 rows: still 4-wave workgroups
     ("bf16", 64, 1, 1, 2049, 300, 29, 300, None),       # 261: 8-wave workgroups
+    ("bf16", 128, 1, 1, 1, 1, 1, 1, None),              # one query, one key
+    ("bf16", 64, 1, 1, 1, 300, 1, 299, None),           # one query against a padded key range
     ("bf16", 128, 1, 1, 300, 300, 2, 300, "random"),
     ("bf16", 128, 2, 2, 260, 260, 2, 258, "blocks"),    # empty/full/partial tiles + padding
     ("bf16", 64, 1, 3, 200, 190, 2, 190, "blocks_b"),   # per-batch masks
